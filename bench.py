@@ -1,0 +1,267 @@
+"""Benchmark of y = x . dequant(W) on one MI355X.
+
+A step is one pass of the whole product path over one batch: the LLaMA-7B
+decode layer set (fused QKV 4096x12288, o_proj 4096x4096, fused gate+up
+4096x22016, down 11008x4096), int4 with fp16 zero-points, group 128, fp16
+activations, M = 1, each layer through wq_gemv.  The headline value is the
+weight bytes (codes + scales + zero-points) streamed per second.
+
+Weights are resident in HBM before timing starts.  Each step uses the next of
+R distinct copies of the layer set (R * 107.5 MB > 1 GiB), so the 256 MB
+last-level cache cannot serve a step from an earlier one: every step streams
+its weights from HBM, as a multi-layer decode does.
+
+Also reported:
+  roofline      the dominant kernel (gate+up GEMV) against HBM bandwidth, from
+                HIP events around each of its launches on its stream, in a
+                second timed pass of the same steps;
+  gemm          the prefill layer set at M = 2048 (symmetric int4, group -1 and
+                128) through wq_gemm, as TFLOP/s against dense fp16 MFMA peak;
+  cpu_baseline  the CPU oracle on a bounded sample of the same step.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, TFLOP/s
+METRIC = "weight GB/s (GEMV, M=1) & TFLOP/s (GEMM, M=2048) as % of HBM/MFMA roofline"
+KERNEL_SOURCES = ["wq_gemv.hip", "wq_decode.hpp", "wq_layout.hpp"]
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--gemm-steps", type=int, default=20)
+    p.add_argument("--no-gemm", action="store_true")
+    p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--copy-probe", action="store_true",
+                   help="also run a plain device copy of known size (counter calibration)")
+    return p.parse_args()
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "weight_only_quantized_w4a16_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(khash):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    counter summary, if it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "gemv_gate_up_m1_counters.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if line.startswith("- ") and ":" in line:
+            k, v = line[2:].split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_sources_sha256_16") != khash:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: every box here has one, and this product path is "
+              f"single-GPU (asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import weight_only_quantized_w4a16_amd as wq
+    import workloads as wl
+
+    if not os.path.exists(wq.LIB_PATH):
+        from weight_only_quantized_w4a16_amd import build as wq_build
+        wq_build.build()
+    wq.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    def to_dev(a, dtype):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(dtype).to(dev)
+        return torch.from_numpy(a.view(np.int32)).to(dev)
+
+    def repack_copies(L, copies):
+        q = to_dev(L.qweight, torch.int32)
+        s = to_dev(L.scales, torch.float16)
+        z = None
+        if L.mode == wl.ZERO_F16:
+            z = to_dev(L.zeros, torch.float16)
+        elif L.mode == wl.ZERO_PACKED:
+            z = to_dev(L.zeros, torch.int32)
+        lut = to_dev(L.lut, torch.float16) if L.lut is not None else None
+        out = [wq.wq_repack(q, s, z, L.mode, L.g_idx, L.K, L.N, L.bits, L.group_size, lut=lut)
+               for _ in range(copies)]
+        del q, s, z
+        return out
+
+    # ---------------- decode layer set (the step) ----------------
+    cfg = wl.CONFIGS[2]
+    M = 1
+    layers = [cfg.layer(name) for (name, _, _) in cfg.layers]
+    set_bytes = sum(L.weight_bytes() for L in layers)
+    R = max(2, -(-(1 << 30) // set_bytes))
+    packed = [repack_copies(L, R) for L in layers]
+    xs = [to_dev(cfg.x(M, L.K), torch.float16) for L in layers]
+    ys = [torch.empty((M, L.N), dtype=torch.float16, device=dev) for L in layers]
+    torch.cuda.synchronize()
+
+    def step(i, events=None):
+        r = i % R
+        for j, L in enumerate(layers):
+            if events is not None:
+                events[j][0].record(stream)
+            wq.wq_gemv(xs[j], packed[j][r], out=ys[j], stream=stream)
+            if events is not None:
+                events[j][1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    value = set_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # per-kernel durations: HIP events around every launch, same steps again
+    per = [[0.0] for _ in layers]
+    nev = min(args.steps, 100)
+    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+            for _ in layers] for _ in range(nev)]
+    for i in range(nev):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    kernel_us = []
+    for j, L in enumerate(layers):
+        t = sum(evs[i][j][0].elapsed_time(evs[i][j][1]) for i in range(nev)) / nev * 1e3
+        kernel_us.append(t)
+    dom = int(np.argmax(kernel_us))
+    Ld = layers[dom]
+    alg_bytes = Ld.weight_bytes() + 2 * M * Ld.K + 2 * M * Ld.N
+    achieved = alg_bytes / (kernel_us[dom] * 1e-6) / 1e9
+    khash = kernel_hash()
+    traffic = read_traffic(khash)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": f"wq_gemv {Ld.name} M={M}", "algorithmic_bytes_per_launch": alg_bytes,
+                "avg_launch_us": round(kernel_us[dom], 3)}
+    per_kernel = {L.name.split("/")[-1]: {"us": round(t, 3), "weight_GBps": round(L.weight_bytes() / (t * 1e-6) / 1e9, 1)}
+                  for L, t in zip(layers, kernel_us)}
+    del packed, xs, ys
+    torch.cuda.empty_cache()
+
+    # ---------------- prefill GEMM at M = 2048 ----------------
+    gemm = None
+    if not args.no_gemm:
+        c3 = wl.CONFIGS[3]
+        Mg = 2048
+        gemm = {}
+        for gs in (-1, 128):
+            gl = [c3.layer(name, 4, gs) for (name, _, _) in c3.layers]
+            gp = [repack_copies(L, 2) for L in gl]
+            gx = [to_dev(c3.x(Mg, L.K), torch.float16) for L in gl]
+            gy = [torch.empty((Mg, L.N), dtype=torch.float16, device=dev) for L in gl]
+            flops = sum(2.0 * Mg * L.N * L.K for L in gl)
+
+            def gstep(i, ev=None):
+                for j in range(len(gl)):
+                    if ev is not None:
+                        ev[j][0].record(stream)
+                    wq.wq_gemm(gx[j], gp[j][i % 2], out=gy[j], stream=stream)
+                    if ev is not None:
+                        ev[j][1].record(stream)
+
+            for i in range(3):
+                gstep(i)
+            torch.cuda.synchronize()
+            a0 = torch.cuda.Event(enable_timing=True)
+            a1 = torch.cuda.Event(enable_timing=True)
+            a0.record(stream)
+            for i in range(args.gemm_steps):
+                gstep(i)
+            a1.record(stream)
+            torch.cuda.synchronize()
+            gms = a0.elapsed_time(a1) / args.gemm_steps
+            tflops = flops / (gms * 1e-3) / 1e12
+            gev = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in gl]
+            gstep(0, gev)
+            torch.cuda.synchronize()
+            gemm[f"group_{gs}"] = {
+                "M": Mg, "ms_per_step": round(gms, 4), "tflops": round(tflops, 1),
+                "peak_tflops": MFMA_F16_PEAK_TFLOPS, "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
+                "per_layer_tflops": {L.name.split("/")[-1]: round(2.0 * Mg * L.N * L.K / (gev[j][0].elapsed_time(gev[j][1]) * 1e-3) / 1e12, 1)
+                                     for j, L in enumerate(gl)}}
+            del gp, gx, gy
+            torch.cuda.empty_cache()
+
+    # ---------------- plain copy (counter calibration) ----------------
+    if args.copy_probe:
+        src = torch.empty(1 << 28, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # ---------------- CPU oracle baseline ----------------
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        xs_h = [cfg.x(M, L.K) for L in layers]
+        reps = 0
+        t0 = time.perf_counter()
+        while True:
+            for L, xh in zip(layers, xs_h):
+                oracle.linear(xh, cfg.dtype, L.qweight, L.scales, L.zeros, L.mode, L.lut, L.g_idx, M, L.N, L.K,
+                              L.bits, L.group_size)
+            reps += 1
+            if time.perf_counter() - t0 >= args.cpu_seconds or reps >= 50:
+                break
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(reps * set_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+               "kind": "oracle",
+               "sample": f"{reps} full passes of the decode layer set (M=1, all columns) in {dt:.1f} s"}
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "llama7b_decode_layer_set_int4_zero_f16_g128_M1",
+                   "layers": [f"{L.name.split('/')[-1]} {L.K}x{L.N}" for L in layers], "M": M,
+                   "weight_bytes_per_step": set_bytes, "rotated_copies": R},
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "roofline": roofline, "per_kernel": per_kernel, "gemm_m2048": gemm, "cpu_baseline": cpu,
+        "kernel_sources_sha256_16": khash,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,162 @@
+/*
+ * wq.h -- C ABI of the weight-only quantized mixed-input matrix product
+ *         y = x . dequant(W)   on AMD Instinct MI355X (gfx950)
+ *
+ * The operation (what every entry point below serves):
+ *   - x is an M x K activation matrix in fp16 or bf16; W is a K x N weight
+ *     matrix stored as 2-, 3- or 4-bit codes (FLUTE page, "How It Works");
+ *   - a weight is decoded on the fly, inside the product, and never written
+ *     back in full precision (Triton GPTQ page, "How It Works"; exllama
+ *     bandwidth discussion, GPTQ paper quote on the quantized-matrix
+ *     full-precision-vector product);
+ *   - uniform modes: w = s * (q - z) with one fp16 scale s per (group, column)
+ *     and a zero-point z that is fixed at 2^(bits-1) (symmetric), stored in
+ *     fp16, or stored as a bits-wide integer (Marlin zero-point issue, replies
+ *     by efrantar and mobicham); group_size -1 means one scale per column;
+ *   - table mode: w = s * T[q] with a per-layer fp16 table T of 2^bits values
+ *     (FLUTE page, "How It Works" and "Highlighted Details");
+ *   - act-order: the group of input row k is g_idx[k] (Triton GPTQ page,
+ *     "Limitations & Caveats");
+ *   - fused QKV / gate+up are the same call on weights concatenated along N
+ *     (Triton GPTQ page, "How It Works").
+ * The dequantised weight is defined as one round-to-nearest-even of the exact
+ * s*(q-z) or s*T[q] to the activation dtype (a reading: the pages give no
+ * formula); wq_dequant_debug produces exactly those bits.
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers named *_host are host memory; every other pointer is device
+ *     memory of the current HIP device.  All buffers are owned by the caller;
+ *     the library allocates nothing and frees nothing.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued asynchronously on it; results are valid once the
+ *     stream has been synchronised.  Only wq_repack synchronises (offline).
+ *   - Errors are returned as wq_status, never thrown.  Arguments are fully
+ *     validated before anything is launched; on any error nothing is written.
+ *   - Shapes: N % 16 == 0; K % 128 == 0 (K % 256 == 0 for 2-bit codes);
+ *     group_size is -1 or a multiple of 32 that divides K and either divides
+ *     or is a multiple of the code tile depth (128 rows; 256 for 2-bit).
+ *     Other shapes return WQ_EUNSUPPORTED.  M == 0 is a valid no-op.
+ *   - Matrices are row-major: x [M][K], y [M][N], scales [G][N], fp16/bf16
+ *     passed as their 16-bit patterns.  G = 1 if group_size == -1 else K/group_size.
+ *
+ * Canonical (input) weight format, read by wq_repack only:
+ *   qweight uint32 [K*bits/32][N]: column n is a little-endian bit stream along
+ *     K, code k at bit offset bits*k over qweight[0][n], qweight[1][n], ...
+ *     (for 4 bits: word r holds rows 8r..8r+7, row 8r+i at bits 4i..4i+3);
+ *   scales fp16 [G][N];
+ *   zeros  fp16 [G][N] (WQ_ZERO_F16) or uint32 [G][N*bits/32] (WQ_ZERO_PACKED,
+ *          row g a little-endian bit stream along N); NULL otherwise;
+ *   g_idx  int32 [K] (act-order) or NULL.
+ */
+#ifndef WQ_H
+#define WQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  WQ_OK = 0,
+  WQ_EINVAL = 1,        /* malformed arguments (NULL where required, bad sizes, bad mode) */
+  WQ_EUNSUPPORTED = 2,  /* well-formed but outside the shapes the kernels cover */
+  WQ_EHIP = 3,          /* a HIP runtime call or kernel launch failed */
+  WQ_ENOSPACE = 4       /* workspace smaller than wq_workspace_bytes() */
+} wq_status;
+
+typedef enum { WQ_F16 = 0, WQ_BF16 = 1 } wq_dtype;
+
+typedef enum {
+  WQ_SYM = 0,           /* z = 2^(bits-1) */
+  WQ_ZERO_F16 = 1,      /* fp16 zero-point per (group, column) */
+  WQ_ZERO_PACKED = 2,   /* bits-wide integer zero-point per (group, column) */
+  WQ_LUT = 3            /* w = s * T[q], fp16 table of 2^bits entries */
+} wq_qmode;
+
+/* Version of the repacked layout; a stored repacked buffer from another
+ * version must be repacked again. */
+#define WQ_LAYOUT_VERSION 1
+int wq_layout_version(void);
+
+const char* wq_status_str(wq_status s);
+
+/*
+ * Size in bytes of the repacked weight buffer (codes + scales + zero-points in
+ * the gfx950 tile layout).  Returns 0 for unsupported arguments.
+ */
+size_t wq_packed_bytes(int K, int N, int bits, int group_size, wq_qmode mode);
+
+/*
+ * Scratch memory wq_gemv / wq_gemm need for a call with these sizes: M*K
+ * activation elements (2 bytes each) when act-order is used (the permuted
+ * copy of x), else 0.
+ */
+size_t wq_workspace_bytes(int M, int N, int K, int bits, int has_perm);
+
+/*
+ * wq_repack -- offline conversion of one quantised layer from the canonical
+ * format to the gfx950 tile layout.  The pages require a kernel-specific
+ * format that any quantiser's output is converted to (Marlin zero-point issue,
+ * efrantar's reply); this is that conversion for these kernels.
+ *
+ *   qweight, scales, zeros : canonical buffers (device), see above
+ *   mode                   : quantisation mode (the code order inside a word
+ *                            differs between uniform and table modes)
+ *   g_idx_host             : act-order group of every row (host, int32 [K]) or
+ *                            NULL.  Each group must hold exactly group_size
+ *                            rows (WQ_EUNSUPPORTED otherwise); rows are stably
+ *                            sorted by group
+ *   packed                 : output, wq_packed_bytes(K, N, bits, group_size, mode)
+ *   perm                   : output (device, int32 [K]) when g_idx_host is given:
+ *                            perm[i] = original row at sorted position i; else
+ *                            ignored (may be NULL)
+ * Synchronises `stream` before returning (the act-order sort runs on the host).
+ */
+wq_status wq_repack(const uint32_t* qweight, const uint16_t* scales, const void* zeros,
+                    wq_qmode mode, const int32_t* g_idx_host, int K, int N, int bits,
+                    int group_size, void* packed, int32_t* perm, void* stream);
+
+/*
+ * wq_dequant_debug -- write the dequantised weight w [K][N] (rows in the
+ * original order, activation dtype `out`) from a repacked buffer.  Test aid:
+ * the result equals, bit for bit, one RNE rounding of s*(q-z) or s*T[q].
+ *   lut  : device fp16 [2^bits] for WQ_LUT, else NULL
+ *   perm : the permutation wq_repack wrote (act-order) or NULL
+ */
+wq_status wq_dequant_debug(const void* packed, wq_qmode mode, const uint16_t* lut,
+                           const int32_t* perm, int K, int N, int bits, int group_size,
+                           wq_dtype out, void* w, void* stream);
+
+/*
+ * wq_gemv -- y [M][N] = x [M][K] . dequant(W), for decode-sized M (1 <= M <= 16;
+ * WQ_EUNSUPPORTED above).  Matrix-vector products are bound by memory
+ * bandwidth and the gain comes from moving fewer weight bytes (exllama
+ * bandwidth discussion, GPTQ paper quote and turboderp's reply); this entry
+ * point streams the packed weight once, split along K inside each workgroup.
+ *   x, y : device, activation dtype `dt` (y in the same dtype), row-major
+ *   packed, lut, perm : as for wq_dequant_debug
+ *   ws   : scratch of at least wq_workspace_bytes(M, N, K, bits, perm != NULL)
+ *          bytes (may be NULL when that is 0)
+ * fp32 accumulation; the output is rounded to `dt` once (RNE).
+ */
+wq_status wq_gemv(const void* x, wq_dtype dt, const void* packed, wq_qmode mode,
+                  const uint16_t* lut, const int32_t* perm, void* y, int M, int N, int K,
+                  int bits, int group_size, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * wq_gemm -- the same product for any M >= 1 (prefill, long context: the
+ * matrix-matrix case the Triton GPTQ page targets, "How It Works"), on MFMA
+ * matrix cores with the activation tile staged in LDS and the weight tile
+ * dequantised in registers.  Same arguments as wq_gemv.
+ */
+wq_status wq_gemm(const void* x, wq_dtype dt, const void* packed, wq_qmode mode,
+                  const uint16_t* lut, const int32_t* perm, void* y, int M, int N, int K,
+                  int bits, int group_size, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WQ_H */

@@ -1,0 +1,124 @@
+"""The C ABI: the library loads, exports every function include/wq.h declares,
+and rejects malformed or unsupported arguments before touching the GPU.
+Runs on the CPU (no compute calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wq.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    import weight_only_quantized_w4a16_amd as wq
+    if not os.path.exists(wq.LIB_PATH):
+        from weight_only_quantized_w4a16_amd import build
+        build.build()
+    return wq.lib()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(wq_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for required in ("wq_repack", "wq_dequant_debug", "wq_gemv", "wq_gemm", "wq_packed_bytes",
+                     "wq_workspace_bytes", "wq_status_str", "wq_layout_version"):
+        assert required in names
+
+
+def test_library_exports_every_declared_function(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings_and_version(L):
+    assert L.wq_layout_version() == 1
+    for s in range(5):
+        assert L.wq_status_str(s)
+
+
+def test_packed_bytes_matches_layout(L):
+    # codes K*N*bits/8, scales G*N*2, zero-points, each section 256-byte aligned
+    al = lambda v: (v + 255) // 256 * 256
+    K, N = 4096, 4096
+    codes = K * N // 2
+    assert L.wq_packed_bytes(K, N, 4, 128, 0) == al(al(codes) + 32 * N * 2)
+    assert L.wq_packed_bytes(K, N, 4, 128, 1) == al(al(al(codes) + 32 * N * 2) + 32 * N * 2)
+    assert L.wq_packed_bytes(K, N, 4, 32, 2) == al(al(al(codes) + 128 * N * 2) + 128 * (N // 16) * 8)
+    assert L.wq_packed_bytes(K, N, 3, -1, 3) == al(al(K * N * 3 // 8) + N * 2)
+    # unsupported / invalid -> 0
+    assert L.wq_packed_bytes(4096, 4104, 4, 128, 0) == 0   # N % 16
+    assert L.wq_packed_bytes(4000, 4096, 4, 128, 0) == 0   # K % 128
+    assert L.wq_packed_bytes(4096, 4096, 5, 128, 0) == 0   # bits
+    assert L.wq_packed_bytes(4096, 4096, 4, 100, 0) == 0   # group does not divide K
+
+
+def test_workspace_bytes(L):
+    assert L.wq_workspace_bytes(16, 4096, 4096, 4, 0) == 0
+    assert L.wq_workspace_bytes(16, 4096, 4096, 4, 1) == 16 * 4096 * 2
+
+
+def call_product(L, fn, M=1, N=4096, K=4096, bits=4, gs=128, mode=0, dt=0, x=16, w=16, y=16, lut=None,
+                 perm=None, ws=None, ws_bytes=0):
+    P = ctypes.c_void_p
+    return getattr(L, fn)(P(x), dt, P(w), mode, P(lut) if lut else None, P(perm) if perm else None, P(y),
+                          M, N, K, bits, gs, P(ws) if ws else None, ws_bytes, None)
+
+
+@pytest.mark.parametrize("fn", ["wq_gemv", "wq_gemm"])
+def test_product_rejects_before_launch(L, fn):
+    # fake, never-dereferenced pointers: validation must return before any launch
+    assert call_product(L, fn, bits=5) == 1                      # WQ_EINVAL
+    assert call_product(L, fn, dt=2) == 1
+    assert call_product(L, fn, mode=7) == 1
+    assert call_product(L, fn, gs=100) == 1                      # group does not divide K
+    assert call_product(L, fn, K=4000) == 1                      # K not a multiple of group
+    assert call_product(L, fn, K=4000, gs=-1) == 2               # K % 128: unsupported
+    assert call_product(L, fn, N=4104) == 2                      # N % 16: unsupported
+    assert call_product(L, fn, M=-1) == 1
+    assert call_product(L, fn, mode=3) == 1                      # table mode without a table
+    assert call_product(L, fn, x=0) == 1                         # NULL activations
+    assert call_product(L, fn, x=8) == 2                         # misaligned
+    assert call_product(L, fn, perm=64) == 4                     # act-order without workspace
+    assert call_product(L, fn, perm=64, ws=64, ws_bytes=10) == 4
+    assert call_product(L, fn, M=0) == 0                         # empty: no-op
+
+
+def test_gemv_rejects_large_m(L):
+    assert call_product(L, "wq_gemv", M=17) == 2
+
+
+def test_repack_rejects_before_launch(L):
+    P = ctypes.c_void_p
+    f = L.wq_repack
+    ok = dict(q=P(16), s=P(16), z=None, mode=0, g=None, K=4096, N=4096, bits=4, gs=128, out=P(16), perm=None)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["q"], a["s"], a["z"], a["mode"], a["g"], a["K"], a["N"], a["bits"], a["gs"], a["out"],
+                 a["perm"], None)
+
+    assert call(q=None) == 1
+    assert call(mode=1) == 1                # fp16 zero-points missing
+    assert call(mode=2, bits=3, N=4112, z=P(16)) == 1  # packed 3-bit zeros need N*3 % 32 == 0
+    assert call(bits=3, K=4000) == 1
+    g = (ctypes.c_int32 * 4096)(*([0] * 4096))
+    assert call(g=ctypes.cast(g, P)) == 1   # g_idx without a perm buffer
+    assert call(g=ctypes.cast(g, P), perm=P(16)) == 2  # unbalanced groups: unsupported
+    bad = (ctypes.c_int32 * 4096)(*([99] * 4096))
+    assert call(g=ctypes.cast(bad, P), perm=P(16)) == 1  # group index out of range
+
+
+def test_dequant_debug_rejects_before_launch(L):
+    P = ctypes.c_void_p
+    f = L.wq_dequant_debug
+    assert f(P(16), 0, None, None, 4096, 4096, 4, 128, 3, P(16), None) == 1   # bad out dtype
+    assert f(P(16), 3, None, None, 4096, 4096, 4, 128, 0, P(16), None) == 1   # table missing
+    assert f(None, 0, None, None, 4096, 4096, 4, 128, 0, P(16), None) == 1

@@ -1,0 +1,80 @@
+"""GPU parity at the full workload sizes, through the same entry points and
+launch shapes the benchmark times.
+
+The oracle computes every output row for a seeded subset of output columns
+(all columns for the single 4096 x 4096 layer); the tolerance is applied over
+that subset.  Workloads (layer shapes of the models the pages measure on, with
+seeded synthetic values, see workloads.py):
+  c1  one 4096 x 4096 layer, int4 symmetric, group 128, fp16, M = 1
+  c2  LLaMA-7B decode layer set, int4 with fp16 zero-points, group 128, M = 1, 4, 16
+  c3  the same shapes at prefill M = 512, 2048, 4096, symmetric, group -1 and 128
+  c4  LLaMA-70B-shaped table-quantised layers, 4/3/2-bit normal-float tables,
+      group 64, bf16, M = 1, 16, 64
+  c5  405B-width act-order layers with packed 4-bit zero-points, group 32,
+      bf16, M = 1, 2, 8, 32, 128, 256
+  g256 4-bit group 256 bf16 regression shape, M = 1, 16, 2048
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from _util import act_dtype, bits_to_tensor, oracle_y, repack_layer, tensor_f64, within_tolerance
+
+pytestmark = pytest.mark.gpu
+
+SAMPLE_COLS = 256
+
+
+@pytest.fixture(scope="module")
+def wq():
+    import weight_only_quantized_w4a16_amd as m
+    m.lib()
+    assert torch.cuda.is_available()
+    return m
+
+
+_layers = {}
+
+
+def get_layer(wq, cfg, lname, bits, gs):
+    key = (cfg.cid, lname, bits, gs)
+    if key not in _layers:
+        _layers.clear()  # keep at most one full-size layer alive
+        L = cfg.layer(lname, bits, gs)
+        _layers[key] = (L, repack_layer(wq, L))
+    return _layers[key]
+
+
+def cases():
+    out = []
+    for cid, cfg in wl.CONFIGS.items():
+        for (lname, K, N) in cfg.layers:
+            for bits in cfg.bits:
+                for gs in cfg.groups:
+                    for M in cfg.Ms:
+                        out.append(pytest.param(cid, lname, bits, gs, M, id=f"{cfg.name}-{lname}-b{bits}-g{gs}-M{M}"))
+    return out
+
+
+@pytest.mark.parametrize("cid,lname,bits,gs,M", cases())
+def test_config_parity(orc, wq, cid, lname, bits, gs, M):
+    cfg = wl.CONFIGS[cid]
+    print(f"[config] {cfg.name} {lname} bits={bits} group={gs} M={M}", flush=True)
+    L, layer = get_layer(wq, cfg, lname, bits, gs)
+    x_bits = cfg.x(M, L.K)
+    x = bits_to_tensor(x_bits, act_dtype(cfg.dtype), "cuda")
+    fn = wq.wq_gemv if M <= 16 else wq.wq_gemm
+    y = fn(x, layer)
+    torch.cuda.synchronize()
+    if L.N * M <= 4096 * 16:
+        cols = None
+        got = tensor_f64(y)
+    else:
+        ncols = SAMPLE_COLS if M <= 512 else 64
+        cols = wl.sample_cols(L.N, ncols, seed=cid * 100 + M)
+        got = tensor_f64(y[:, torch.from_numpy(cols).long().cuda()])
+    ref = oracle_y(orc, x_bits, cfg.dtype, L, cols)
+    ok, err, bound = within_tolerance(got, ref)
+    assert ok, f"max error {err:.3e} > bound {bound:.3e}"
+    assert np.all(np.isfinite(got))

@@ -1,0 +1,176 @@
+"""Weight-only quantized mixed-input matmul y = x . dequant(W) on MI355X (gfx950).
+
+Thin ctypes binding over libwq.so (the C ABI in include/wq.h).  Every function
+here only marshals arguments -- torch tensors supply device memory and the
+current HIP stream -- and calls the library; every step of the product runs in
+the library's HIP kernels.  There is no CPU fallback: if libwq.so is missing or
+cannot be loaded, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+import torch
+
+SYM, ZERO_F16, ZERO_PACKED, LUT = 0, 1, 2, 3
+F16, BF16 = 0, 1
+LAYOUT_VERSION = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libwq.so")
+
+_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "HIP error", 4: "workspace too small"}
+
+_lib = None
+
+
+class WQError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {_STATUS.get(status, status)} (status {status})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libwq.so (built by __graft_entry__.build() or weight_only_quantized_w4a16_amd/build.py)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run weight_only_quantized_w4a16_amd/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        L.wq_layout_version.restype = I
+        L.wq_status_str.argtypes = [I]
+        L.wq_status_str.restype = ctypes.c_char_p
+        L.wq_packed_bytes.argtypes = [I, I, I, I, I]
+        L.wq_packed_bytes.restype = Z
+        L.wq_workspace_bytes.argtypes = [I, I, I, I, I]
+        L.wq_workspace_bytes.restype = Z
+        L.wq_repack.argtypes = [P, P, P, I, P, I, I, I, I, P, P, P]
+        L.wq_repack.restype = I
+        L.wq_dequant_debug.argtypes = [P, I, P, P, I, I, I, I, I, P, P]
+        L.wq_dequant_debug.restype = I
+        for name in ("wq_gemv", "wq_gemm"):
+            f = getattr(L, name)
+            f.argtypes = [P, I, P, I, P, P, P, I, I, I, I, I, P, Z, P]
+            f.restype = I
+        if L.wq_layout_version() != LAYOUT_VERSION:
+            raise RuntimeError("libwq.so layout version does not match this binding")
+        _lib = L
+    return _lib
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(fn: str, rc: int):
+    if rc != 0:
+        raise WQError(fn, rc)
+
+
+def _dt(dtype: torch.dtype) -> int:
+    if dtype == torch.float16:
+        return F16
+    if dtype == torch.bfloat16:
+        return BF16
+    raise ValueError(f"activation dtype must be float16 or bfloat16, got {dtype}")
+
+
+def _torch_dt(dt: int) -> torch.dtype:
+    return torch.float16 if dt == F16 else torch.bfloat16
+
+
+def wq_packed_bytes(K: int, N: int, bits: int, group_size: int, mode: int) -> int:
+    return int(lib().wq_packed_bytes(K, N, bits, group_size, mode))
+
+
+def wq_workspace_bytes(M: int, N: int, K: int, bits: int, has_perm: bool) -> int:
+    return int(lib().wq_workspace_bytes(M, N, K, bits, int(bool(has_perm))))
+
+
+@dataclasses.dataclass
+class PackedLayer:
+    """A repacked layer: the library's tile-layout buffer plus its description."""
+    packed: torch.Tensor                 # uint8 device buffer (codes + scales + zero-points)
+    K: int
+    N: int
+    bits: int
+    group_size: int
+    mode: int
+    lut: Optional[torch.Tensor] = None   # fp16 [2^bits] (table mode)
+    perm: Optional[torch.Tensor] = None  # int32 [K] (act-order)
+
+
+def wq_repack(qweight: torch.Tensor, scales: torch.Tensor, zeros: Optional[torch.Tensor], mode: int,
+              g_idx, K: int, N: int, bits: int, group_size: int, lut: Optional[torch.Tensor] = None,
+              stream=None) -> PackedLayer:
+    """Canonical GPTQ-style tensors (device: qweight int32 [K*bits/32][N], scales fp16
+    [G][N], zeros fp16 [G][N] or int32 [G][N*bits/32]) -> PackedLayer.  g_idx: host
+    int32 array-like [K] or None."""
+    dev = qweight.device
+    nbytes = wq_packed_bytes(K, N, bits, group_size, mode)
+    if nbytes == 0:
+        raise WQError("wq_packed_bytes", 2)
+    packed = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    perm = None
+    g_host = None
+    if g_idx is not None:
+        import numpy as np
+        g_host = np.ascontiguousarray(torch.as_tensor(g_idx).cpu().numpy(), dtype=np.int32)
+        perm = torch.empty(K, dtype=torch.int32, device=dev)
+    rc = lib().wq_repack(_ptr(qweight), _ptr(scales), _ptr(zeros), mode,
+                         None if g_host is None else ctypes.c_void_p(g_host.ctypes.data),
+                         K, N, bits, group_size, _ptr(packed), _ptr(perm), _stream(stream))
+    _check("wq_repack", rc)
+    return PackedLayer(packed, K, N, bits, group_size, mode, lut, perm)
+
+
+def wq_dequant_debug(layer: PackedLayer, dtype: torch.dtype, stream=None) -> torch.Tensor:
+    w = torch.empty((layer.K, layer.N), dtype=dtype, device=layer.packed.device)
+    rc = lib().wq_dequant_debug(_ptr(layer.packed), layer.mode, _ptr(layer.lut), _ptr(layer.perm),
+                                layer.K, layer.N, layer.bits, layer.group_size, _dt(dtype), _ptr(w),
+                                _stream(stream))
+    _check("wq_dequant_debug", rc)
+    return w
+
+
+def _product(fn: str, x: torch.Tensor, layer: PackedLayer, out: Optional[torch.Tensor],
+             ws: Optional[torch.Tensor], stream) -> torch.Tensor:
+    if x.dim() != 2 or x.shape[1] != layer.K or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [M][K] tensor")
+    M = x.shape[0]
+    if out is None:
+        out = torch.empty((M, layer.N), dtype=x.dtype, device=x.device)
+    need = wq_workspace_bytes(M, layer.N, layer.K, layer.bits, layer.perm is not None)
+    if need and (ws is None or ws.numel() * ws.element_size() < need):
+        ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+    rc = getattr(lib(), fn)(_ptr(x), _dt(x.dtype), _ptr(layer.packed), layer.mode, _ptr(layer.lut),
+                            _ptr(layer.perm), _ptr(out), M, layer.N, layer.K, layer.bits,
+                            layer.group_size, _ptr(ws) if need else None,
+                            need if need else 0, _stream(stream))
+    _check(fn, rc)
+    return out
+
+
+def wq_gemv(x: torch.Tensor, layer: PackedLayer, out=None, ws=None, stream=None) -> torch.Tensor:
+    """y = x . dequant(W) for 1 <= M <= 16 (decode)."""
+    return _product("wq_gemv", x, layer, out, ws, stream)
+
+
+def wq_gemm(x: torch.Tensor, layer: PackedLayer, out=None, ws=None, stream=None) -> torch.Tensor:
+    """y = x . dequant(W) for any M (prefill)."""
+    return _product("wq_gemm", x, layer, out, ws, stream)
+
+
+def linear(x: torch.Tensor, layer: PackedLayer, out=None, ws=None, stream=None) -> torch.Tensor:
+    """Decode-sized M goes to wq_gemv, larger M to wq_gemm."""
+    return (wq_gemv if x.shape[0] <= 16 else wq_gemm)(x, layer, out, ws, stream)

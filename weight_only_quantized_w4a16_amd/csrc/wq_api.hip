@@ -1,0 +1,325 @@
+// wq_api.hip -- C entry points: validation, offline repack, debug dequant,
+// act-order gather, dispatch of the product kernels.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <vector>
+
+#include "wq_common.hpp"
+#include "wq_decode.hpp"
+
+using namespace wq;
+
+// ---------------------------------------------------------------------------
+// Repack kernels
+// ---------------------------------------------------------------------------
+
+// Code of row k of column n in the canonical layout (column = little-endian
+// bit stream along K, word r at qweight[r][n]).
+template <int BITS>
+__device__ inline uint32_t canonical_code(const uint32_t* qw, int N, int n, int k) {
+  const uint32_t bit = (uint32_t)BITS * (uint32_t)k;
+  const uint32_t r = bit >> 5, sh = bit & 31;
+  uint32_t v = qw[(size_t)r * N + n] >> sh;
+  if (sh + BITS > 32) v |= qw[(size_t)(r + 1) * N + n] << (32 - sh);
+  return v & ((1u << BITS) - 1u);
+}
+
+// Place code q of element e, k-block kb into a lane's words (see wq_layout.hpp).
+template <int BITS, bool TABLE_LAYOUT>
+__device__ inline void place_code(uint32_t* w, int kb, int e, uint32_t q) {
+  if (BITS == 4) {
+    const int nib = TABLE_LAYOUT ? e : (e % 2) * 4 + e / 2;
+    w[kb] |= q << (4 * nib);
+  } else if (BITS == 2) {
+    const int i = 4 * (kb % 2) + e / 2;
+    const int pos = TABLE_LAYOUT ? 4 * i + 2 * (e % 2) : 16 * (e % 2) + 2 * i;
+    w[kb / 2] |= q << pos;
+  } else {
+    const int p = 4 * kb + e / 2;
+    const int fb = 3 * (e % 2);  // bit offset of this code inside the 6-bit pair field
+    if (p < 15) {
+      w[p / 5] |= q << (6 * (p % 5) + fb);
+    } else {
+      for (int b = 0; b < 3; ++b) {
+        const int fbit = fb + b;
+        w[fbit / 2] |= ((q >> b) & 1u) << (30 + fbit % 2);
+      }
+    }
+  }
+}
+
+// One thread per lane-slot of a tile: grid (ktiles, ntiles), block 64.
+template <int BITS, bool TABLE_LAYOUT>
+__global__ void repack_codes_kernel(const uint32_t* __restrict__ qw, const int32_t* __restrict__ perm,
+                                    int N, int ktiles, uint32_t* __restrict__ out) {
+  constexpr int KT = BITS == 2 ? 256 : 128;
+  constexpr int KB = KT / 32;
+  constexpr int WPL = BITS == 3 ? 3 : 4;
+  const int lane = threadIdx.x, kt = blockIdx.x, nt = blockIdx.y;
+  const int c = lane & 15, h = lane >> 4;
+  const int n = nt * 16 + c;
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  for (int kb = 0; kb < KB; ++kb) {
+    for (int e = 0; e < 8; ++e) {
+      const int row = kt * KT + 32 * kb + 8 * h + e;
+      const int k = perm ? perm[row] : row;
+      place_code<BITS, TABLE_LAYOUT>(w, kb, e, canonical_code<BITS>(qw, N, n, k));
+    }
+  }
+  uint32_t* dst = out + (((size_t)nt * ktiles + kt) * 64 + lane) * WPL;
+  for (int j = 0; j < WPL; ++j) dst[j] = w[j];
+}
+
+// Scales and fp16 zero-points: [G][N] -> [N/16][G][16].  grid (G, ntiles), block 16.
+__global__ void repack_meta16_kernel(const uint16_t* __restrict__ src, int N, int G, uint16_t* __restrict__ dst) {
+  const int c = threadIdx.x, g = blockIdx.x, nt = blockIdx.y;
+  dst[((size_t)nt * G + g) * 16 + c] = src[(size_t)g * N + nt * 16 + c];
+}
+
+// Packed zero-points: canonical row g = bit stream along N of BITS-wide codes
+// -> 16 nibbles per (column tile, group).  grid (G, ntiles), block 1... 64.
+template <int BITS>
+__global__ void repack_zeros_packed_kernel(const uint32_t* __restrict__ zp, int N, int G, int ntiles,
+                                           uint32_t* __restrict__ dst) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;  // (nt, g) pair
+  if (i >= ntiles * G) return;
+  const int nt = i / G, g = i % G;
+  const size_t wpr = (size_t)N * BITS / 32;
+  uint32_t lo = 0, hi = 0;
+  for (int c = 0; c < 16; ++c) {
+    const uint32_t bit = (uint32_t)BITS * (uint32_t)(nt * 16 + c);
+    const uint32_t r = bit >> 5, sh = bit & 31;
+    uint32_t v = zp[g * wpr + r] >> sh;
+    if (sh + BITS > 32) v |= zp[g * wpr + r + 1] << (32 - sh);
+    v &= (1u << BITS) - 1u;
+    if (c < 8) lo |= v << (4 * c); else hi |= v << (4 * (c - 8));
+  }
+  dst[((size_t)nt * G + g) * 2 + 0] = lo;
+  dst[((size_t)nt * G + g) * 2 + 1] = hi;
+}
+
+// ---------------------------------------------------------------------------
+// Debug dequantisation: one wave per tile, exact path (the one the large-M
+// product uses), written back in the original row order.
+// ---------------------------------------------------------------------------
+template <int BITS, int DT, int MODE>
+__global__ __launch_bounds__(64) void dequant_debug_kernel(const uint8_t* __restrict__ packed, Layout L,
+                                                          const uint16_t* __restrict__ lut,
+                                                          const int32_t* __restrict__ perm,
+                                                          uint16_t* __restrict__ w) {
+  constexpr int KT = BITS == 2 ? 256 : 128;
+  constexpr int KB = KT / 32;
+  constexpr int WPL = BITS == 3 ? 3 : 4;
+  __shared__ uint32_t table[MODE == LUT ? (32 << (2 * BITS)) : 1];
+  const int lane = threadIdx.x, kt = blockIdx.x, nt = blockIdx.y;
+  const int c = lane & 15, h = lane >> 4;
+  if constexpr (MODE == LUT) {
+    fill_pair_table<BITS, false>(table, lut, lane, 64);
+    __syncthreads();
+  }
+  const uint32_t* tab = table + (lane & 31);
+  const uint32_t* src = (const uint32_t*)(packed + L.codes_off) + (((size_t)nt * L.ktiles + kt) * 64 + lane) * WPL;
+  uint32_t words[4] = {0u, 0u, 0u, 0u};
+  for (int j = 0; j < WPL; ++j) words[j] = src[j];
+  const uint16_t* S = (const uint16_t*)(packed + L.scales_off);
+  const void* Z = packed + L.zeros_off;
+  const int n = nt * 16 + c;
+  sfor<KB>([&](auto kbc) {
+    constexpr int kb = decltype(kbc)::value;
+    const int row0 = kt * KT + 32 * kb + 8 * h;
+    const int g = row0 / L.gsz;
+    ExactParams p;
+    p.s = load_scale(S, L.G, nt, g, c);
+    p.s_h = h2s(p.s);
+    p.sz = MODE == LUT ? 0.0f : p.s * load_zero<MODE, BITS>(Z, L.G, nt, g, c);
+    const u32x4 v = exact_frag<BITS, DT, MODE, kb>(words, p, tab);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int row = row0 + e;
+      const int k = perm ? perm[row] : row;
+      const uint32_t pair = v[e / 2];
+      w[(size_t)k * L.N + n] = (uint16_t)((e % 2) ? (pair >> 16) : (pair & 0xFFFFu));
+    }
+  });
+}
+
+// Act-order: xp[m][i] = x[m][perm[i]].
+__global__ void gather_x_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ perm, int M, int K,
+                                uint16_t* __restrict__ xp) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (size_t)M * K) return;
+  const size_t m = i / K, k = i % K;
+  xp[i] = x[m * K + perm[k]];
+}
+
+// ---------------------------------------------------------------------------
+// C entry points
+// ---------------------------------------------------------------------------
+extern "C" {
+
+int wq_layout_version(void) { return WQ_LAYOUT_VERSION; }
+
+const char* wq_status_str(wq_status s) {
+  switch (s) {
+    case WQ_OK: return "ok";
+    case WQ_EINVAL: return "invalid argument";
+    case WQ_EUNSUPPORTED: return "unsupported shape or configuration";
+    case WQ_EHIP: return "HIP runtime error";
+    case WQ_ENOSPACE: return "workspace too small";
+  }
+  return "unknown status";
+}
+
+size_t wq_packed_bytes(int K, int N, int bits, int group_size, wq_qmode mode) {
+  if (check_layer(K, N, bits, group_size, mode) != WQ_OK) return 0;
+  return make_layout(K, N, bits, group_size, mode).total;
+}
+
+size_t wq_workspace_bytes(int M, int N, int K, int bits, int has_perm) {
+  (void)N; (void)bits;
+  if (M <= 0 || K <= 0 || !has_perm) return 0;
+  return (size_t)M * K * 2;
+}
+
+wq_status wq_repack(const uint32_t* qweight, const uint16_t* scales, const void* zeros, wq_qmode mode,
+                    const int32_t* g_idx_host, int K, int N, int bits, int group_size, void* packed,
+                    int32_t* perm, void* stream) {
+  wq_status st = check_layer(K, N, bits, group_size, mode);
+  if (st != WQ_OK) return st;
+  if (!qweight || !scales || !packed) return WQ_EINVAL;
+  if ((mode == ZERO_F16 || mode == ZERO_PACKED) && !zeros) return WQ_EINVAL;
+  if (mode == ZERO_PACKED && ((long)N * bits) % 32 != 0) return WQ_EINVAL;
+  if (g_idx_host && !perm) return WQ_EINVAL;
+  const Layout L = make_layout(K, N, bits, group_size, mode);
+  hipStream_t s = (hipStream_t)stream;
+
+  // Act-order: stable sort of rows by group; every group must hold gsz rows.
+  std::vector<int32_t> host_perm;
+  if (g_idx_host) {
+    std::vector<int> count(L.G, 0);
+    for (int k = 0; k < K; ++k) {
+      const int g = g_idx_host[k];
+      if (g < 0 || g >= L.G) return WQ_EINVAL;
+      ++count[g];
+    }
+    for (int g = 0; g < L.G; ++g)
+      if (count[g] != L.gsz) return WQ_EUNSUPPORTED;
+    std::vector<int> next(L.G);
+    for (int g = 0; g < L.G; ++g) next[g] = g * L.gsz;
+    host_perm.resize(K);
+    for (int k = 0; k < K; ++k) host_perm[next[g_idx_host[k]]++] = k;
+    if (hipMemcpyAsync(perm, host_perm.data(), sizeof(int32_t) * K, hipMemcpyHostToDevice, s) != hipSuccess)
+      return WQ_EHIP;
+  }
+  const int32_t* dperm = g_idx_host ? perm : nullptr;
+  uint8_t* out = (uint8_t*)packed;
+  const bool table_layout = mode == LUT;
+  dim3 grid(L.ktiles, L.ntiles);
+#define WQ_REPACK_CODES(B)                                                                              \
+  if (table_layout)                                                                                     \
+    hipLaunchKernelGGL((repack_codes_kernel<B, true>), grid, dim3(64), 0, s, qweight, dperm, N, L.ktiles, \
+                       (uint32_t*)(out + L.codes_off));                                                 \
+  else                                                                                                  \
+    hipLaunchKernelGGL((repack_codes_kernel<B, false>), grid, dim3(64), 0, s, qweight, dperm, N, L.ktiles, \
+                       (uint32_t*)(out + L.codes_off));
+  if (bits == 4) { WQ_REPACK_CODES(4) }
+  else if (bits == 3) { WQ_REPACK_CODES(3) }
+  else { WQ_REPACK_CODES(2) }
+#undef WQ_REPACK_CODES
+  hipLaunchKernelGGL(repack_meta16_kernel, dim3(L.G, L.ntiles), dim3(16), 0, s, scales, N, L.G,
+                     (uint16_t*)(out + L.scales_off));
+  if (mode == ZERO_F16) {
+    hipLaunchKernelGGL(repack_meta16_kernel, dim3(L.G, L.ntiles), dim3(16), 0, s, (const uint16_t*)zeros, N, L.G,
+                       (uint16_t*)(out + L.zeros_off));
+  } else if (mode == ZERO_PACKED) {
+    const int pairs = L.G * L.ntiles;
+    dim3 g2((pairs + 255) / 256);
+    if (bits == 4)
+      hipLaunchKernelGGL(repack_zeros_packed_kernel<4>, g2, dim3(256), 0, s, (const uint32_t*)zeros, N, L.G,
+                         L.ntiles, (uint32_t*)(out + L.zeros_off));
+    else if (bits == 3)
+      hipLaunchKernelGGL(repack_zeros_packed_kernel<3>, g2, dim3(256), 0, s, (const uint32_t*)zeros, N, L.G,
+                         L.ntiles, (uint32_t*)(out + L.zeros_off));
+    else
+      hipLaunchKernelGGL(repack_zeros_packed_kernel<2>, g2, dim3(256), 0, s, (const uint32_t*)zeros, N, L.G,
+                         L.ntiles, (uint32_t*)(out + L.zeros_off));
+  }
+  if ((st = launch_status()) != WQ_OK) return st;
+  // host_perm is read by the copy above: wait before it goes out of scope.
+  return hipStreamSynchronize(s) == hipSuccess ? WQ_OK : WQ_EHIP;
+}
+
+wq_status wq_dequant_debug(const void* packed, wq_qmode mode, const uint16_t* lut, const int32_t* perm, int K,
+                           int N, int bits, int group_size, wq_dtype out, void* w, void* stream) {
+  wq_status st = check_layer(K, N, bits, group_size, mode);
+  if (st != WQ_OK) return st;
+  if (!packed || !w) return WQ_EINVAL;
+  if (out != WQ_F16 && out != WQ_BF16) return WQ_EINVAL;
+  if (mode == LUT && !lut) return WQ_EINVAL;
+  const Layout L = make_layout(K, N, bits, group_size, mode);
+  hipStream_t s = (hipStream_t)stream;
+  dim3 grid(L.ktiles, L.ntiles);
+  bool launched = false;
+  sfor<3>([&](auto bi) {
+    constexpr int B = decltype(bi)::value + 2;
+    if (B != bits) return;
+    sfor<2>([&](auto di) {
+      constexpr int D = decltype(di)::value;
+      if (D != (int)out) return;
+      sfor<4>([&](auto mi) {
+        constexpr int MODE = decltype(mi)::value;
+        if (MODE != (int)mode) return;
+        hipLaunchKernelGGL((dequant_debug_kernel<B, D, MODE>), grid, dim3(64), 0, s, (const uint8_t*)packed, L,
+                           lut, perm, (uint16_t*)w);
+        launched = true;
+      });
+    });
+  });
+  if (!launched) return WQ_EINVAL;
+  return launch_status();
+}
+
+static wq_status product(bool gemm, const void* x, wq_dtype dt, const void* packed, wq_qmode mode,
+                         const uint16_t* lut, const int32_t* perm, void* y, int M, int N, int K, int bits,
+                         int group_size, void* ws, size_t ws_bytes, void* stream) {
+  wq_status st = check_layer(K, N, bits, group_size, mode);
+  if (st != WQ_OK) return st;
+  if (M < 0) return WQ_EINVAL;
+  if (dt != WQ_F16 && dt != WQ_BF16) return WQ_EINVAL;
+  if (!gemm && M > 16) return WQ_EUNSUPPORTED;
+  if (M == 0) return WQ_OK;
+  if (!x || !packed || !y) return WQ_EINVAL;
+  if (mode == LUT && !lut) return WQ_EINVAL;
+  if (((uintptr_t)x | (uintptr_t)y | (uintptr_t)packed) & 15) return WQ_EUNSUPPORTED;
+  if (M > (1 << 24)) return WQ_EUNSUPPORTED;
+  const size_t need = wq_workspace_bytes(M, N, K, bits, perm != nullptr);
+  if (need && (!ws || ws_bytes < need)) return WQ_ENOSPACE;
+  if (need && ((uintptr_t)ws & 15)) return WQ_EUNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  const void* xin = x;
+  if (perm) {
+    const size_t total = (size_t)M * K;
+    hipLaunchKernelGGL(gather_x_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
+                       (const uint16_t*)x, perm, M, K, (uint16_t*)ws);
+    if ((st = launch_status()) != WQ_OK) return st;
+    xin = ws;
+  }
+  ProductArgs a{xin, (int)dt, packed, (int)mode, lut, y, M, N, K, bits, group_size, s};
+  return launch_product(gemm, a);
+}
+
+wq_status wq_gemv(const void* x, wq_dtype dt, const void* packed, wq_qmode mode, const uint16_t* lut,
+                  const int32_t* perm, void* y, int M, int N, int K, int bits, int group_size, void* ws,
+                  size_t ws_bytes, void* stream) {
+  return product(false, x, dt, packed, mode, lut, perm, y, M, N, K, bits, group_size, ws, ws_bytes, stream);
+}
+
+wq_status wq_gemm(const void* x, wq_dtype dt, const void* packed, wq_qmode mode, const uint16_t* lut,
+                  const int32_t* perm, void* y, int M, int N, int K, int bits, int group_size, void* ws,
+                  size_t ws_bytes, void* stream) {
+  return product(true, x, dt, packed, mode, lut, perm, y, M, N, K, bits, group_size, ws, ws_bytes, stream);
+}
+
+}  // extern "C"

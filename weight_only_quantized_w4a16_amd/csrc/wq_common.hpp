@@ -1,0 +1,96 @@
+// wq_common.hpp -- host-side helpers shared by the entry points.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <type_traits>
+#include <utility>
+
+#include "../../include/wq.h"
+#include "wq_layout.hpp"
+
+namespace wq {
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I = 0..N-1.
+template <typename F, int... I>
+__host__ __device__ inline void sfor_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__host__ __device__ inline void sfor(F&& f) {
+  sfor_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Validation shared by every entry point that reads a repacked layer.
+inline wq_status check_layer(int K, int N, int bits, int group_size, int mode) {
+  if (K <= 0 || N <= 0) return WQ_EINVAL;
+  if (bits != 2 && bits != 3 && bits != 4) return WQ_EINVAL;
+  if (mode < SYM || mode > LUT) return WQ_EINVAL;
+  if (group_size != -1 && (group_size <= 0 || K % group_size != 0)) return WQ_EINVAL;
+  if (K > (1 << 24) || N > (1 << 24)) return WQ_EUNSUPPORTED;
+  if (N % 16 != 0 || K % tile_k(bits) != 0) return WQ_EUNSUPPORTED;
+  const int gsz = group_size == -1 ? K : group_size;
+  if (gsz % 32 != 0) return WQ_EUNSUPPORTED;
+  const int kt = tile_k(bits);
+  if (gsz % kt != 0 && kt % gsz != 0) return WQ_EUNSUPPORTED;
+  return WQ_OK;
+}
+
+inline wq_status launch_status() {
+  return hipGetLastError() == hipSuccess ? WQ_OK : WQ_EHIP;
+}
+
+// Entry points of the product kernels (validated arguments only).
+struct ProductArgs {
+  const void* x;            // activations [M][K] (already permuted for act-order)
+  int dt;
+  const void* packed;
+  int mode;
+  const uint16_t* lut;
+  void* y;
+  int M, N, K, bits, group_size;
+  hipStream_t stream;
+};
+#define WQ_CAT2(a, b) a##b
+#define WQ_CAT(a, b) WQ_CAT2(a, b)
+#define WQ_DECLARE_VARIANT(v)                      \
+  wq_status launch_gemv_##v(const ProductArgs& a); \
+  wq_status launch_gemm_##v(const ProductArgs& a);
+WQ_DECLARE_VARIANT(f16_b2)
+WQ_DECLARE_VARIANT(f16_b3)
+WQ_DECLARE_VARIANT(f16_b4)
+WQ_DECLARE_VARIANT(bf16_b2)
+WQ_DECLARE_VARIANT(bf16_b3)
+WQ_DECLARE_VARIANT(bf16_b4)
+#undef WQ_DECLARE_VARIANT
+
+// The kernel files are compiled once per variant with WQ_DT / WQ_BITS set.
+#if defined(WQ_DT) && defined(WQ_BITS)
+#if WQ_DT == 0 && WQ_BITS == 2
+#define WQ_VARIANT f16_b2
+#elif WQ_DT == 0 && WQ_BITS == 3
+#define WQ_VARIANT f16_b3
+#elif WQ_DT == 0 && WQ_BITS == 4
+#define WQ_VARIANT f16_b4
+#elif WQ_DT == 1 && WQ_BITS == 2
+#define WQ_VARIANT bf16_b2
+#elif WQ_DT == 1 && WQ_BITS == 3
+#define WQ_VARIANT bf16_b3
+#else
+#define WQ_VARIANT bf16_b4
+#endif
+#endif
+
+inline wq_status launch_product(bool gemm, const ProductArgs& a) {
+#define WQ_PICK(v) return gemm ? launch_gemm_##v(a) : launch_gemv_##v(a)
+  if (a.dt == F16) {
+    if (a.bits == 2) WQ_PICK(f16_b2);
+    if (a.bits == 3) WQ_PICK(f16_b3);
+    WQ_PICK(f16_b4);
+  }
+  if (a.bits == 2) WQ_PICK(bf16_b2);
+  if (a.bits == 3) WQ_PICK(bf16_b3);
+  WQ_PICK(bf16_b4);
+#undef WQ_PICK
+}
+
+}  // namespace wq

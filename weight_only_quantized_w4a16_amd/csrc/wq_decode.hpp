@@ -1,0 +1,274 @@
+// wq_decode.hpp -- in-register decoding of packed codes into MFMA B operands.
+//
+// Codes are turned into 16-bit floats in registers and fed straight to the
+// matrix cores; nothing is written back (Triton GPTQ page, "How It Works";
+// exllama bandwidth discussion, GPTQ paper quote).  Three decoders:
+//
+//  * offset decode (uniform modes, used by the decode-sized product): OR-ing a
+//    code into the mantissa of a float whose exponent makes the unit in the
+//    last place 1 yields (bias + q) exactly.  fp16: bias 1024 (0x6400), one
+//    packed fp16 add or fma removes it, giving q - 2^(bits-1) exactly.  bf16:
+//    bias 128 (0x4300) is kept; the caller corrects with the row sums of x.
+//    The fp16 variant may scale a field sitting 4^i higher by 4^-i in the same
+//    fma, which saves shifts.
+//  * table decode: two codes form an index into an LDS table of value pairs
+//    (FLUTE page, "How It Works": value = table entry times scale).  The
+//    table is replicated 32 times so that lane l always reads bank l%32.
+//  * exact decode (the large-M product and the debug dump): the dequantised
+//    weight RN(s*(q - z)) or RN(s*T[q]) in the activation dtype, one rounding
+//    of a value that is exact in fp32 (s has 11 significant bits, q - z at most
+//    13 for fp16 zero-points in the ranges used, T[q] 11).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "wq_layout.hpp"
+
+namespace wq {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+__device__ inline uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ inline h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
+__device__ inline h2 h2s(float a) { return h2{(_Float16)a, (_Float16)a}; }
+
+__device__ inline float f16_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+__device__ inline float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+__device__ inline uint16_t f32_to_f16(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+__device__ inline uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+// Round a pair of fp32 values (each exactly representable in fp32) to the
+// activation dtype with round-to-nearest-even; lo in bits 0..15.
+template <int DT>
+__device__ inline uint32_t pack2(float lo, float hi) {
+  if constexpr (DT == F16) {
+    return (uint32_t)f32_to_f16(lo) | ((uint32_t)f32_to_f16(hi) << 16);
+  } else {
+    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  }
+}
+
+template <int DT>
+__device__ inline f4 mfma16(u32x4 a, u32x4 b, f4 c) {
+  if constexpr (DT == F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, a), __builtin_bit_cast(h8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, a), __builtin_bit_cast(bf8, b), c, 0, 0, 0);
+}
+
+// 1.0 in every element: B operand that turns an MFMA into row sums of A.
+template <int DT>
+__device__ inline u32x4 ones_frag() {
+  const uint32_t one = DT == F16 ? 0x3C003C00u : 0x3F803F80u;
+  return u32x4{one, one, one, one};
+}
+
+constexpr uint32_t kMagicF16 = 0x64006400u;   // fp16 1024 in both halves
+constexpr uint32_t kMagicBF16 = 0x43004300u;  // bf16 128 in both halves
+
+// ---------------------------------------------------------------------------
+// Field extraction for the 3-bit layout: pair p (0..15) of a tile lane.
+// ---------------------------------------------------------------------------
+template <int P>
+__device__ inline uint32_t pair6(const uint32_t* w) {
+  if constexpr (P < 15) {
+    return (w[P / 5] >> (6 * (P % 5))) & 0x3Fu;
+  } else {
+    return (w[0] >> 30) | ((w[1] >> 30) << 2) | ((w[2] >> 30) << 4);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Offset decode: B operand (8 values of one k-block) for uniform modes.
+//   fp16: values are q - 2^(BITS-1)  (exact small integers)
+//   bf16: values are 128 + q         (exact; caller subtracts 128 + z later)
+// ---------------------------------------------------------------------------
+template <int BITS, int DT, int KB>
+__device__ inline u32x4 offset_frag(const uint32_t* w) {
+  u32x4 r;
+  if constexpr (BITS == 4) {
+    const uint32_t x = w[KB];
+    if constexpr (DT == F16) {
+      const float off = 1024.0f + 8.0f;
+      const uint32_t x8 = x >> 8;
+      r[0] = as_u32(as_h2((x & 0x000F000Fu) | kMagicF16) - h2s(off));
+      r[1] = as_u32(__builtin_elementwise_fma(as_h2((x & 0x00F000F0u) | kMagicF16), h2s(1.0f / 16), h2s(-(64.0f + 8.0f))));
+      r[2] = as_u32(as_h2((x8 & 0x000F000Fu) | kMagicF16) - h2s(off));
+      r[3] = as_u32(__builtin_elementwise_fma(as_h2((x8 & 0x00F000F0u) | kMagicF16), h2s(1.0f / 16), h2s(-(64.0f + 8.0f))));
+    } else {
+      r[0] = (x & 0x000F000Fu) | kMagicBF16;
+      r[1] = ((x >> 4) & 0x000F000Fu) | kMagicBF16;
+      r[2] = ((x >> 8) & 0x000F000Fu) | kMagicBF16;
+      r[3] = ((x >> 12) & 0x000F000Fu) | kMagicBF16;
+    }
+  } else if constexpr (BITS == 2) {
+    const uint32_t x = w[KB / 2];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = 4 * (KB % 2) + q;  // pair index inside the word
+      if constexpr (DT == F16) {
+        const int ii = i < 5 ? i : i - 5;
+        const uint32_t xs = i < 5 ? x : (x >> 10);
+        const float sc = 1.0f / (float)(1 << (2 * ii));
+        r[q] = as_u32(__builtin_elementwise_fma(as_h2((xs & (0x00030003u << (2 * ii))) | kMagicF16), h2s(sc),
+                                                h2s(-(1024.0f * sc + 2.0f))));
+      } else {
+        r[q] = ((x >> (2 * i)) & 0x00030003u) | kMagicBF16;
+      }
+    }
+  } else {  // BITS == 3
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t f;
+      switch (4 * KB + q) {
+        case 0: f = pair6<0>(w); break;   case 1: f = pair6<1>(w); break;
+        case 2: f = pair6<2>(w); break;   case 3: f = pair6<3>(w); break;
+        case 4: f = pair6<4>(w); break;   case 5: f = pair6<5>(w); break;
+        case 6: f = pair6<6>(w); break;   case 7: f = pair6<7>(w); break;
+        case 8: f = pair6<8>(w); break;   case 9: f = pair6<9>(w); break;
+        case 10: f = pair6<10>(w); break; case 11: f = pair6<11>(w); break;
+        case 12: f = pair6<12>(w); break; case 13: f = pair6<13>(w); break;
+        case 14: f = pair6<14>(w); break; default: f = pair6<15>(w); break;
+      }
+      const uint32_t v = (f & 7u) | ((f & 0x38u) << 13);
+      if constexpr (DT == F16)
+        r[q] = as_u32(as_h2(v | kMagicF16) - h2s(1024.0f + 4.0f));
+      else
+        r[q] = v | kMagicBF16;
+    }
+  }
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// Table decode: B operand from an LDS pair table.  tab points at the table's
+// column for this lane (base + (lane % 32)); entry idx sits at tab[idx * 32].
+// ---------------------------------------------------------------------------
+template <int BITS, int KB>
+__device__ inline u32x4 table_frag(const uint32_t* w, const uint32_t* tab) {
+  u32x4 r;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t idx;
+    if constexpr (BITS == 4) {
+      idx = (w[KB] >> (8 * q)) & 0xFFu;
+    } else if constexpr (BITS == 2) {
+      idx = (w[KB / 2] >> (4 * (4 * (KB % 2) + q))) & 0xFu;
+    } else {
+      switch (4 * KB + q) {
+        case 0: idx = pair6<0>(w); break;   case 1: idx = pair6<1>(w); break;
+        case 2: idx = pair6<2>(w); break;   case 3: idx = pair6<3>(w); break;
+        case 4: idx = pair6<4>(w); break;   case 5: idx = pair6<5>(w); break;
+        case 6: idx = pair6<6>(w); break;   case 7: idx = pair6<7>(w); break;
+        case 8: idx = pair6<8>(w); break;   case 9: idx = pair6<9>(w); break;
+        case 10: idx = pair6<10>(w); break; case 11: idx = pair6<11>(w); break;
+        case 12: idx = pair6<12>(w); break; case 13: idx = pair6<13>(w); break;
+        case 14: idx = pair6<14>(w); break; default: idx = pair6<15>(w); break;
+      }
+    }
+    r[q] = tab[idx * 32];
+  }
+  return r;
+}
+
+// Fill an LDS pair table: entry idx = value[lo] | value[hi] << 16 with
+// lo = idx & (2^BITS - 1), hi = idx >> BITS, replicated over 32 columns.
+// AS_BF16: store RN_bf16(T) instead of the fp16 T.
+template <int BITS, bool AS_BF16>
+__device__ inline void fill_pair_table(uint32_t* table, const uint16_t* lut, int tid, int nthreads) {
+  constexpr int n = 1 << (2 * BITS);
+  constexpr int mask = (1 << BITS) - 1;
+  for (int i = tid; i < n * 32; i += nthreads) {
+    const int idx = i >> 5;
+    uint16_t lo = lut[idx & mask], hi = lut[idx >> BITS];
+    if (AS_BF16) {
+      lo = f32_to_bf16(f16_to_f32(lo));
+      hi = f32_to_bf16(f16_to_f32(hi));
+    }
+    table[i] = (uint32_t)lo | ((uint32_t)hi << 16);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Code of element E (0..7) of k-block KB, for the generic exact path.
+// ---------------------------------------------------------------------------
+template <int BITS, bool TABLE_LAYOUT, int KB, int E>
+__device__ inline uint32_t code_at(const uint32_t* w) {
+  if constexpr (BITS == 4) {
+    constexpr int nib = TABLE_LAYOUT ? E : (E % 2) * 4 + E / 2;
+    return (w[KB] >> (4 * nib)) & 0xFu;
+  } else if constexpr (BITS == 2) {
+    constexpr int i = 4 * (KB % 2) + E / 2;
+    constexpr int pos = TABLE_LAYOUT ? 4 * i + 2 * (E % 2) : 16 * (E % 2) + 2 * i;
+    return (w[KB / 2] >> pos) & 0x3u;
+  } else {
+    const uint32_t f = pair6<(4 * KB + E / 2) % 16>(w);
+    return (E % 2) ? (f >> 3) : (f & 7u);
+  }
+}
+
+// Zero-point / table parameters of one (group, column) for the exact path.
+struct ExactParams {
+  float s;        // scale
+  float sz;       // s * z (exact in fp32)
+  h2 s_h;         // scale as an fp16 pair (fp16 fast paths)
+};
+
+// Exact dequantised B operand for k-block KB: RN_dt(s*(q - z)) or RN_dt(s*T[q]).
+// tab: LDS fp16 pair table column for this lane (table mode only).
+template <int BITS, int DT, int MODE, int KB>
+__device__ inline u32x4 exact_frag(const uint32_t* w, const ExactParams& p, const uint32_t* tab) {
+  u32x4 r;
+  if constexpr (MODE == SYM && DT == F16) {
+    // q - 2^(b-1) is exact in fp16; one fp16 multiply rounds s*(q-z) once.
+    const u32x4 o = offset_frag<BITS, F16, KB>(w);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r[q] = as_u32(as_h2(o[q]) * p.s_h);
+  } else if constexpr (MODE == LUT && DT == F16) {
+    const u32x4 t = table_frag<BITS, KB>(w, tab);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r[q] = as_u32(as_h2(t[q]) * p.s_h);
+  } else if constexpr (MODE == LUT) {
+    const u32x4 t = table_frag<BITS, KB>(w, tab);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const h2 v = as_h2(t[q]);
+      r[q] = pack2<DT>(p.s * (float)v[0], p.s * (float)v[1]);
+    }
+  } else {
+    constexpr bool TL = false;
+    const float c[8] = {(float)code_at<BITS, TL, KB, 0>(w), (float)code_at<BITS, TL, KB, 1>(w),
+                        (float)code_at<BITS, TL, KB, 2>(w), (float)code_at<BITS, TL, KB, 3>(w),
+                        (float)code_at<BITS, TL, KB, 4>(w), (float)code_at<BITS, TL, KB, 5>(w),
+                        (float)code_at<BITS, TL, KB, 6>(w), (float)code_at<BITS, TL, KB, 7>(w)};
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      r[q] = pack2<DT>(__builtin_fmaf(c[2 * q], p.s, -p.sz), __builtin_fmaf(c[2 * q + 1], p.s, -p.sz));
+  }
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// Scale / zero-point loads from the re-laid metadata.
+// ---------------------------------------------------------------------------
+__device__ inline float load_scale(const uint16_t* S, int G, int nt, int g, int c) {
+  return f16_to_f32(S[((size_t)nt * G + g) * 16 + c]);
+}
+
+template <int MODE, int BITS>
+__device__ inline float load_zero(const void* Z, int G, int nt, int g, int c) {
+  if constexpr (MODE == ZERO_F16) {
+    return f16_to_f32(((const uint16_t*)Z)[((size_t)nt * G + g) * 16 + c]);
+  } else if constexpr (MODE == ZERO_PACKED) {
+    const uint32_t word = ((const uint32_t*)Z)[((size_t)nt * G + g) * 2 + (c >> 3)];
+    return (float)((word >> (4 * (c & 7))) & 0xFu);
+  } else {
+    return (float)(1 << (BITS - 1));
+  }
+}
+
+}  // namespace wq

@@ -1,0 +1,81 @@
+// wq_layout.hpp -- geometry of the gfx950 tile layout of a repacked layer.
+//
+// The pages only say a kernel consumes weights in its own format, produced
+// offline from whatever the quantiser wrote (Marlin zero-point issue,
+// efrantar's reply).  This is that format for the MFMA-based kernels here.
+//
+// Codes.  The weight is cut into tiles of 16 columns x KT rows (KT = 128 for
+// 3- and 4-bit codes, 256 for 2-bit codes).  Tiles are stored column-tile
+// major ([N/16][K/KT]), so one wave streaming down K for one column tile
+// reads contiguous memory.  Inside a tile, lane l (0..63) of a wave owns
+// WPL consecutive 32-bit words (WPL = 4, or 3 for 3-bit codes): one 128-bit
+// (96-bit) coalesced load per lane, 1 KiB (768 B) per wave.  Lane l = 16h + c
+// holds column c of the tile and, for every 32-row k-block kb of the tile,
+// rows 32kb + 8h + e (e = 0..7): exactly the B operand a 16x16x32 MFMA wants
+// from that lane.  Rows are in act-order-sorted order when a permutation is
+// used.
+//
+// Element e of k-block kb inside the lane's words:
+//   4-bit uniform  word kb, nibble (e%2)*4 + e/2   (pairs (e, e+1) sit in the
+//                  two 16-bit halves, so one AND/OR makes two fp16 values)
+//   4-bit table    word kb, nibble e               (a byte is a code pair)
+//   2-bit uniform  word kb/2, bits 16*(e%2) + 2*i,  i = 4*(kb%2) + e/2
+//   2-bit table    word kb/2, bits 4*i + 2*(e%2)    (a nibble is a code pair)
+//   3-bit (both)   pair p = 4*kb + e/2 is the 6-bit field lo | hi << 3
+//                  (lo = even element); pairs 0..14 at bits 6*(p%5) of word
+//                  p/5, pair 15 split over bits 30..31 of words 0, 1, 2.
+//
+// Scales / zero-points.  Re-laid column-tile major: fp16 [N/16][G][16]; fp16
+// zero-points the same; packed zero-points as 16 nibbles (one per column of
+// the tile, whatever the code width) in two words: uint32 [N/16][G][2].
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+#define WQ_HD __host__ __device__ inline
+
+namespace wq {
+
+enum { SYM = 0, ZERO_F16 = 1, ZERO_PACKED = 2, LUT = 3 };
+enum { F16 = 0, BF16 = 1 };
+
+WQ_HD int tile_k(int bits) { return bits == 2 ? 256 : 128; }
+WQ_HD int words_per_lane(int bits) { return bits == 3 ? 3 : 4; }
+WQ_HD int tile_bytes(int bits) { return 256 * words_per_lane(bits); }
+WQ_HD int kblocks_per_tile(int bits) { return tile_k(bits) / 32; }
+
+struct Layout {
+  int K, N, bits, group_size, mode;
+  int G;        // number of groups
+  int gsz;      // rows per group (K for group_size == -1)
+  int ktiles;   // K / tile_k
+  int ntiles;   // N / 16
+  size_t codes_off, codes_bytes;
+  size_t scales_off, scales_bytes;
+  size_t zeros_off, zeros_bytes;
+  size_t total;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Valid only for arguments the API has already validated.
+inline Layout make_layout(int K, int N, int bits, int group_size, int mode) {
+  Layout L;
+  L.K = K; L.N = N; L.bits = bits; L.group_size = group_size; L.mode = mode;
+  L.gsz = group_size == -1 ? K : group_size;
+  L.G = K / L.gsz;
+  L.ktiles = K / tile_k(bits);
+  L.ntiles = N / 16;
+  L.codes_off = 0;
+  L.codes_bytes = (size_t)L.ntiles * L.ktiles * tile_bytes(bits);
+  L.scales_off = align256(L.codes_bytes);
+  L.scales_bytes = (size_t)L.G * N * 2;
+  L.zeros_off = align256(L.scales_off + L.scales_bytes);
+  if (mode == ZERO_F16) L.zeros_bytes = (size_t)L.G * N * 2;
+  else if (mode == ZERO_PACKED) L.zeros_bytes = (size_t)L.G * L.ntiles * 8;
+  else L.zeros_bytes = 0;
+  L.total = align256(L.zeros_off + L.zeros_bytes);
+  return L;
+}
+
+}  // namespace wq
