@@ -77,7 +77,7 @@ typedef enum {
 
 /* Version of the repacked layout; a stored repacked buffer from another
  * version must be repacked again. */
-#define WQ_LAYOUT_VERSION 1
+#define WQ_LAYOUT_VERSION 2
 int wq_layout_version(void);
 
 const char* wq_status_str(wq_status s);

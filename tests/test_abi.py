@@ -39,7 +39,7 @@ def test_library_exports_every_declared_function(L):
 
 
 def test_status_strings_and_version(L):
-    assert L.wq_layout_version() == 1
+    assert L.wq_layout_version() == 2
     for s in range(5):
         assert L.wq_status_str(s)
 
@@ -50,7 +50,7 @@ def test_packed_bytes_matches_layout(L):
     K, N = 4096, 4096
     codes = K * N // 2
     assert L.wq_packed_bytes(K, N, 4, 128, 0) == al(al(codes) + 32 * N * 2)
-    assert L.wq_packed_bytes(K, N, 4, 128, 1) == al(al(al(codes) + 32 * N * 2) + 32 * N * 2)
+    assert L.wq_packed_bytes(K, N, 4, 128, 1) == al(al(codes) + 32 * N * 4)  # (scale, zero) pairs
     assert L.wq_packed_bytes(K, N, 4, 32, 2) == al(al(al(codes) + 128 * N * 2) + 128 * (N // 16) * 8)
     assert L.wq_packed_bytes(K, N, 3, -1, 3) == al(al(K * N * 3 // 8) + N * 2)
     # unsupported / invalid -> 0

@@ -17,7 +17,7 @@ import torch
 
 SYM, ZERO_F16, ZERO_PACKED, LUT = 0, 1, 2, 3
 F16, BF16 = 0, 1
-LAYOUT_VERSION = 1
+LAYOUT_VERSION = 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libwq.so")

@@ -72,32 +72,39 @@ __global__ void repack_codes_kernel(const uint32_t* __restrict__ qw, const int32
   for (int j = 0; j < WPL; ++j) dst[j] = w[j];
 }
 
-// Scales and fp16 zero-points: [G][N] -> [N/16][G][16].  grid (G, ntiles), block 16.
-__global__ void repack_meta16_kernel(const uint16_t* __restrict__ src, int N, int G, uint16_t* __restrict__ dst) {
-  const int c = threadIdx.x, g = blockIdx.x, nt = blockIdx.y;
-  dst[((size_t)nt * G + g) * 16 + c] = src[(size_t)g * N + nt * 16 + c];
+// Scale records: [G][N] (+ fp16 zero-points [G][N]) -> [N/16][R][16][GPU]
+// (pairs (s, z) when zeros16 is given).  grid (R, ntiles), block 16 * gpu.
+__global__ void repack_scales_kernel(const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros16,
+                                     int N, int nrec, int gpu, void* __restrict__ dst) {
+  const int c = threadIdx.x / gpu, j = threadIdx.x % gpu, rec = blockIdx.x, nt = blockIdx.y;
+  const int g = rec * gpu + j;
+  const size_t src = (size_t)g * N + nt * 16 + c;
+  const size_t o = (((size_t)nt * nrec + rec) * 16 + c) * gpu + j;
+  if (zeros16)
+    ((uint32_t*)dst)[o] = (uint32_t)scales[src] | ((uint32_t)zeros16[src] << 16);
+  else
+    ((uint16_t*)dst)[o] = scales[src];
 }
 
 // Packed zero-points: canonical row g = bit stream along N of BITS-wide codes
-// -> 16 nibbles per (column tile, group).  grid (G, ntiles), block 1... 64.
+// -> per (column tile, record, half, group in record) one word of 8 nibbles.
 template <int BITS>
-__global__ void repack_zeros_packed_kernel(const uint32_t* __restrict__ zp, int N, int G, int ntiles,
+__global__ void repack_zeros_packed_kernel(const uint32_t* __restrict__ zp, int N, int nrec, int gpu, int ntiles,
                                            uint32_t* __restrict__ dst) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;  // (nt, g) pair
-  if (i >= ntiles * G) return;
-  const int nt = i / G, g = i % G;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;  // ((nt * nrec + rec) * 2 + half) * gpu + j
+  if (i >= ntiles * nrec * 2 * gpu) return;
+  const int j = i % gpu, half = (i / gpu) % 2, rec = (i / (2 * gpu)) % nrec, nt = i / (2 * gpu * nrec);
+  const int g = rec * gpu + j;
   const size_t wpr = (size_t)N * BITS / 32;
-  uint32_t lo = 0, hi = 0;
-  for (int c = 0; c < 16; ++c) {
-    const uint32_t bit = (uint32_t)BITS * (uint32_t)(nt * 16 + c);
+  uint32_t word = 0;
+  for (int c = 0; c < 8; ++c) {
+    const uint32_t bit = (uint32_t)BITS * (uint32_t)(nt * 16 + 8 * half + c);
     const uint32_t r = bit >> 5, sh = bit & 31;
     uint32_t v = zp[g * wpr + r] >> sh;
     if (sh + BITS > 32) v |= zp[g * wpr + r + 1] << (32 - sh);
-    v &= (1u << BITS) - 1u;
-    if (c < 8) lo |= v << (4 * c); else hi |= v << (4 * (c - 8));
+    word |= (v & ((1u << BITS) - 1u)) << (4 * c);
   }
-  dst[((size_t)nt * G + g) * 2 + 0] = lo;
-  dst[((size_t)nt * G + g) * 2 + 1] = hi;
+  dst[i] = word;
 }
 
 // ---------------------------------------------------------------------------
@@ -120,21 +127,36 @@ __global__ __launch_bounds__(64) void dequant_debug_kernel(const uint8_t* __rest
     __syncthreads();
   }
   const uint32_t* tab = table + (lane & 31);
+  const DecodeConsts dk = make_decode_consts<DT>();
   const uint32_t* src = (const uint32_t*)(packed + L.codes_off) + (((size_t)nt * L.ktiles + kt) * 64 + lane) * WPL;
   uint32_t words[4] = {0u, 0u, 0u, 0u};
   for (int j = 0; j < WPL; ++j) words[j] = src[j];
-  const uint16_t* S = (const uint16_t*)(packed + L.scales_off);
-  const void* Z = packed + L.zeros_off;
+  const uint8_t* S = packed + L.scales_off;
+  const uint32_t* Z = (const uint32_t*)(packed + L.zeros_off);
   const int n = nt * 16 + c;
   sfor<KB>([&](auto kbc) {
     constexpr int kb = decltype(kbc)::value;
     const int row0 = kt * KT + 32 * kb + 8 * h;
-    const int g = row0 / L.gsz;
+    const int unit = row0 / 128;
+    const int rec = meta_record(unit, L.gsz);
+    const int j = L.gpu > 1 ? (row0 % 128) / L.gsz : 0;  // group inside the record
+    const size_t ri = (((size_t)nt * L.nrec + rec) * 16 + c) * L.gpu + j;
+    float sv, zv;
+    if (MODE == ZERO_F16) {
+      const uint32_t w2 = ((const uint32_t*)S)[ri];
+      sv = f16_to_f32((uint16_t)(w2 & 0xFFFFu));
+      zv = f16_to_f32((uint16_t)(w2 >> 16));
+    } else {
+      sv = f16_to_f32(((const uint16_t*)S)[ri]);
+      zv = MODE == ZERO_PACKED
+               ? rec_zero_packed(Z + (((size_t)nt * L.nrec + rec) * 2 + (c >> 3)) * L.gpu, j, c)
+               : (float)(1 << (BITS - 1));
+    }
     ExactParams p;
-    p.s = load_scale(S, L.G, nt, g, c);
+    p.s = sv;
     p.s_h = h2s(p.s);
-    p.sz = MODE == LUT ? 0.0f : p.s * load_zero<MODE, BITS>(Z, L.G, nt, g, c);
-    const u32x4 v = exact_frag<BITS, DT, MODE, kb>(words, p, tab);
+    p.sz = MODE == LUT ? 0.0f : p.s * zv;
+    const u32x4 v = exact_frag<BITS, DT, MODE, kb>(words, p, tab, dk);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int row = row0 + e;
@@ -228,23 +250,21 @@ wq_status wq_repack(const uint32_t* qweight, const uint16_t* scales, const void*
   else if (bits == 3) { WQ_REPACK_CODES(3) }
   else { WQ_REPACK_CODES(2) }
 #undef WQ_REPACK_CODES
-  hipLaunchKernelGGL(repack_meta16_kernel, dim3(L.G, L.ntiles), dim3(16), 0, s, scales, N, L.G,
-                     (uint16_t*)(out + L.scales_off));
-  if (mode == ZERO_F16) {
-    hipLaunchKernelGGL(repack_meta16_kernel, dim3(L.G, L.ntiles), dim3(16), 0, s, (const uint16_t*)zeros, N, L.G,
-                       (uint16_t*)(out + L.zeros_off));
-  } else if (mode == ZERO_PACKED) {
-    const int pairs = L.G * L.ntiles;
-    dim3 g2((pairs + 255) / 256);
+  hipLaunchKernelGGL(repack_scales_kernel, dim3(L.nrec, L.ntiles), dim3(16 * L.gpu), 0, s, scales,
+                     mode == ZERO_F16 ? (const uint16_t*)zeros : nullptr, N, L.nrec, L.gpu,
+                     (void*)(out + L.scales_off));
+  if (mode == ZERO_PACKED) {
+    const int words = L.ntiles * L.nrec * 2 * L.gpu;
+    dim3 g2((words + 255) / 256);
     if (bits == 4)
-      hipLaunchKernelGGL(repack_zeros_packed_kernel<4>, g2, dim3(256), 0, s, (const uint32_t*)zeros, N, L.G,
-                         L.ntiles, (uint32_t*)(out + L.zeros_off));
+      hipLaunchKernelGGL(repack_zeros_packed_kernel<4>, g2, dim3(256), 0, s, (const uint32_t*)zeros, N, L.nrec,
+                         L.gpu, L.ntiles, (uint32_t*)(out + L.zeros_off));
     else if (bits == 3)
-      hipLaunchKernelGGL(repack_zeros_packed_kernel<3>, g2, dim3(256), 0, s, (const uint32_t*)zeros, N, L.G,
-                         L.ntiles, (uint32_t*)(out + L.zeros_off));
+      hipLaunchKernelGGL(repack_zeros_packed_kernel<3>, g2, dim3(256), 0, s, (const uint32_t*)zeros, N, L.nrec,
+                         L.gpu, L.ntiles, (uint32_t*)(out + L.zeros_off));
     else
-      hipLaunchKernelGGL(repack_zeros_packed_kernel<2>, g2, dim3(256), 0, s, (const uint32_t*)zeros, N, L.G,
-                         L.ntiles, (uint32_t*)(out + L.zeros_off));
+      hipLaunchKernelGGL(repack_zeros_packed_kernel<2>, g2, dim3(256), 0, s, (const uint32_t*)zeros, N, L.nrec,
+                         L.gpu, L.ntiles, (uint32_t*)(out + L.zeros_off));
   }
   if ((st = launch_status()) != WQ_OK) return st;
   // host_perm is read by the copy above: wait before it goes out of scope.

@@ -32,6 +32,9 @@ inline wq_status check_layer(int K, int N, int bits, int group_size, int mode) {
   if (gsz % 32 != 0) return WQ_EUNSUPPORTED;
   const int kt = tile_k(bits);
   if (gsz % kt != 0 && kt % gsz != 0) return WQ_EUNSUPPORTED;
+  // every section of the repacked buffer must stay below 2 GiB (buffer offsets)
+  if ((size_t)K * N * bits / 8 >= ((size_t)1 << 31) || (size_t)(K / gsz) * N * 2 >= ((size_t)1 << 31))
+    return WQ_EUNSUPPORTED;
   return WQ_OK;
 }
 

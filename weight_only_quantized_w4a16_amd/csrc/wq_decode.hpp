@@ -4,13 +4,13 @@
 // matrix cores; nothing is written back (Triton GPTQ page, "How It Works";
 // exllama bandwidth discussion, GPTQ paper quote).  Three decoders:
 //
-//  * offset decode (uniform modes, used by the decode-sized product): OR-ing a
-//    code into the mantissa of a float whose exponent makes the unit in the
-//    last place 1 yields (bias + q) exactly.  fp16: bias 1024 (0x6400), one
-//    packed fp16 add or fma removes it, giving q - 2^(bits-1) exactly.  bf16:
-//    bias 128 (0x4300) is kept; the caller corrects with the row sums of x.
-//    The fp16 variant may scale a field sitting 4^i higher by 4^-i in the same
-//    fma, which saves shifts.
+//  * offset decode (uniform modes): OR-ing a code into the mantissa of a float
+//    whose exponent makes the unit in the last place 1 yields (bias + q)
+//    exactly.  The biased form keeps that value (bias 1024 for fp16, 0x6400;
+//    128 for bf16, 0x4300) and the decode-sized product removes bias + z
+//    after the MFMA with the row sums of x.  The offset form (fp16) removes the
+//    bias with one packed fp16 add or fma, giving q - 2^(bits-1) exactly; the
+//    fma may also scale a field sitting 4^i higher by 4^-i, which saves shifts.
 //  * table decode: two codes form an index into an LDS table of value pairs
 //    (FLUTE page, "How It Works": value = table entry times scale).  The
 //    table is replicated 32 times so that lane l always reads bank l%32.
@@ -31,6 +31,16 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer resources: a load whose offset lies past num_records returns zero
+// without touching memory, which lets prefetches past the end of a range stay
+// unconditional (straight-line code keeps the wait counters exact).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOutOfRange = 0x80000000u;  // every buffer here is smaller than 2 GiB
+__device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+constexpr int kNontemporal = 2;  // cache policy of the streamed weight loads
 
 __device__ inline uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
 __device__ inline h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
@@ -70,6 +80,33 @@ __device__ inline u32x4 ones_frag() {
 constexpr uint32_t kMagicF16 = 0x64006400u;   // fp16 1024 in both halves
 constexpr uint32_t kMagicBF16 = 0x43004300u;  // bf16 128 in both halves
 
+// Operands of the offset decode, held in registers the compiler cannot see
+// through.  gfx9 VOP3 encodings take no literal constants and at most one
+// scalar operand; with the masks in scalar registers and the exponent pattern
+// in a vector register, (w & mask) | magic becomes one v_and_or_b32 instead
+// of an AND and an OR.  Built once per kernel (the empty asm emits nothing).
+struct DecodeConsts {
+  uint32_t m4lo, m4hi;  // 0x000F000F, 0x00F000F0
+  uint32_t m2[5];       // 0x00030003 << 2i
+  uint32_t magic;       // kMagicF16 or kMagicBF16
+};
+
+template <int DT>
+__device__ inline DecodeConsts make_decode_consts() {
+  DecodeConsts k;
+  k.m4lo = 0x000F000Fu;
+  k.m4hi = 0x00F000F0u;
+#pragma unroll
+  for (int i = 0; i < 5; ++i) k.m2[i] = 0x00030003u << (2 * i);
+  k.magic = DT == F16 ? kMagicF16 : kMagicBF16;
+  asm volatile("" : "+s"(k.m4lo));
+  asm volatile("" : "+s"(k.m4hi));
+#pragma unroll
+  for (int i = 0; i < 5; ++i) asm volatile("" : "+s"(k.m2[i]));
+  asm volatile("" : "+v"(k.magic));
+  return k;
+}
+
 // ---------------------------------------------------------------------------
 // Field extraction for the 3-bit layout: pair p (0..15) of a tile lane.
 // ---------------------------------------------------------------------------
@@ -88,22 +125,22 @@ __device__ inline uint32_t pair6(const uint32_t* w) {
 //   bf16: values are 128 + q         (exact; caller subtracts 128 + z later)
 // ---------------------------------------------------------------------------
 template <int BITS, int DT, int KB>
-__device__ inline u32x4 offset_frag(const uint32_t* w) {
+__device__ inline u32x4 offset_frag(const uint32_t* w, const DecodeConsts& k) {
   u32x4 r;
   if constexpr (BITS == 4) {
     const uint32_t x = w[KB];
     if constexpr (DT == F16) {
       const float off = 1024.0f + 8.0f;
       const uint32_t x8 = x >> 8;
-      r[0] = as_u32(as_h2((x & 0x000F000Fu) | kMagicF16) - h2s(off));
-      r[1] = as_u32(__builtin_elementwise_fma(as_h2((x & 0x00F000F0u) | kMagicF16), h2s(1.0f / 16), h2s(-(64.0f + 8.0f))));
-      r[2] = as_u32(as_h2((x8 & 0x000F000Fu) | kMagicF16) - h2s(off));
-      r[3] = as_u32(__builtin_elementwise_fma(as_h2((x8 & 0x00F000F0u) | kMagicF16), h2s(1.0f / 16), h2s(-(64.0f + 8.0f))));
+      r[0] = as_u32(as_h2((x & k.m4lo) | k.magic) - h2s(off));
+      r[1] = as_u32(__builtin_elementwise_fma(as_h2((x & k.m4hi) | k.magic), h2s(1.0f / 16), h2s(-(64.0f + 8.0f))));
+      r[2] = as_u32(as_h2((x8 & k.m4lo) | k.magic) - h2s(off));
+      r[3] = as_u32(__builtin_elementwise_fma(as_h2((x8 & k.m4hi) | k.magic), h2s(1.0f / 16), h2s(-(64.0f + 8.0f))));
     } else {
-      r[0] = (x & 0x000F000Fu) | kMagicBF16;
-      r[1] = ((x >> 4) & 0x000F000Fu) | kMagicBF16;
-      r[2] = ((x >> 8) & 0x000F000Fu) | kMagicBF16;
-      r[3] = ((x >> 12) & 0x000F000Fu) | kMagicBF16;
+      r[0] = (x & k.m4lo) | k.magic;
+      r[1] = ((x >> 4) & k.m4lo) | k.magic;
+      r[2] = ((x >> 8) & k.m4lo) | k.magic;
+      r[3] = ((x >> 12) & k.m4lo) | k.magic;
     }
   } else if constexpr (BITS == 2) {
     const uint32_t x = w[KB / 2];
@@ -114,10 +151,10 @@ __device__ inline u32x4 offset_frag(const uint32_t* w) {
         const int ii = i < 5 ? i : i - 5;
         const uint32_t xs = i < 5 ? x : (x >> 10);
         const float sc = 1.0f / (float)(1 << (2 * ii));
-        r[q] = as_u32(__builtin_elementwise_fma(as_h2((xs & (0x00030003u << (2 * ii))) | kMagicF16), h2s(sc),
+        r[q] = as_u32(__builtin_elementwise_fma(as_h2((xs & k.m2[ii]) | k.magic), h2s(sc),
                                                 h2s(-(1024.0f * sc + 2.0f))));
       } else {
-        r[q] = ((x >> (2 * i)) & 0x00030003u) | kMagicBF16;
+        r[q] = ((x >> (2 * i)) & k.m2[0]) | k.magic;
       }
     }
   } else {  // BITS == 3
@@ -136,9 +173,47 @@ __device__ inline u32x4 offset_frag(const uint32_t* w) {
       }
       const uint32_t v = (f & 7u) | ((f & 0x38u) << 13);
       if constexpr (DT == F16)
-        r[q] = as_u32(as_h2(v | kMagicF16) - h2s(1024.0f + 4.0f));
+        r[q] = as_u32(as_h2(v | k.magic) - h2s(1024.0f + 4.0f));
       else
-        r[q] = v | kMagicBF16;
+        r[q] = v | k.magic;
+    }
+  }
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// Biased decode (decode-sized product): B = bias + q exactly for either dtype
+// (bias 1024 for fp16, 128 for bf16), one shift and one AND-OR per register
+// and no float arithmetic; the caller removes bias + z with the row sums of x.
+// ---------------------------------------------------------------------------
+template <int BITS, int KB>
+__device__ inline u32x4 biased_frag(const uint32_t* w, const DecodeConsts& k) {
+  u32x4 r;
+  if constexpr (BITS == 4) {
+    const uint32_t x = w[KB];
+    r[0] = (x & k.m4lo) | k.magic;
+    r[1] = ((x >> 4) & k.m4lo) | k.magic;
+    r[2] = ((x >> 8) & k.m4lo) | k.magic;
+    r[3] = ((x >> 12) & k.m4lo) | k.magic;
+  } else if constexpr (BITS == 2) {
+    const uint32_t x = w[KB / 2];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r[q] = ((x >> (2 * (4 * (KB % 2) + q))) & k.m2[0]) | k.magic;
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t f;
+      switch (4 * KB + q) {
+        case 0: f = pair6<0>(w); break;   case 1: f = pair6<1>(w); break;
+        case 2: f = pair6<2>(w); break;   case 3: f = pair6<3>(w); break;
+        case 4: f = pair6<4>(w); break;   case 5: f = pair6<5>(w); break;
+        case 6: f = pair6<6>(w); break;   case 7: f = pair6<7>(w); break;
+        case 8: f = pair6<8>(w); break;   case 9: f = pair6<9>(w); break;
+        case 10: f = pair6<10>(w); break; case 11: f = pair6<11>(w); break;
+        case 12: f = pair6<12>(w); break; case 13: f = pair6<13>(w); break;
+        case 14: f = pair6<14>(w); break; default: f = pair6<15>(w); break;
+      }
+      r[q] = (f & 7u) | ((f & 0x38u) << 13) | k.magic;
     }
   }
   return r;
@@ -221,11 +296,12 @@ struct ExactParams {
 // Exact dequantised B operand for k-block KB: RN_dt(s*(q - z)) or RN_dt(s*T[q]).
 // tab: LDS fp16 pair table column for this lane (table mode only).
 template <int BITS, int DT, int MODE, int KB>
-__device__ inline u32x4 exact_frag(const uint32_t* w, const ExactParams& p, const uint32_t* tab) {
+__device__ inline u32x4 exact_frag(const uint32_t* w, const ExactParams& p, const uint32_t* tab,
+                                   const DecodeConsts& k) {
   u32x4 r;
   if constexpr (MODE == SYM && DT == F16) {
     // q - 2^(b-1) is exact in fp16; one fp16 multiply rounds s*(q-z) once.
-    const u32x4 o = offset_frag<BITS, F16, KB>(w);
+    const u32x4 o = offset_frag<BITS, F16, KB>(w, k);
 #pragma unroll
     for (int q = 0; q < 4; ++q) r[q] = as_u32(as_h2(o[q]) * p.s_h);
   } else if constexpr (MODE == LUT && DT == F16) {
@@ -253,22 +329,36 @@ __device__ inline u32x4 exact_frag(const uint32_t* w, const ExactParams& p, cons
 }
 
 // ---------------------------------------------------------------------------
-// Scale / zero-point loads from the re-laid metadata.
+// Metadata records (see wq_layout.hpp).  A record is loaded as REC bytes
+// into words; accessors pick group j of the record.
 // ---------------------------------------------------------------------------
-__device__ inline float load_scale(const uint16_t* S, int G, int nt, int g, int c) {
-  return f16_to_f32(S[((size_t)nt * G + g) * 16 + c]);
+template <int BYTES>
+__device__ inline void load_record(rsrc_t r, uint32_t voff, uint32_t soff, uint32_t* dst) {
+  if constexpr (BYTES == 2) {
+    dst[0] = __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+  } else if constexpr (BYTES == 4) {
+    dst[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+  } else if constexpr (BYTES == 8) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+    dst[0] = v[0]; dst[1] = v[1];
+  } else {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    dst[0] = v[0]; dst[1] = v[1]; dst[2] = v[2]; dst[3] = v[3];
+  }
 }
 
-template <int MODE, int BITS>
-__device__ inline float load_zero(const void* Z, int G, int nt, int g, int c) {
-  if constexpr (MODE == ZERO_F16) {
-    return f16_to_f32(((const uint16_t*)Z)[((size_t)nt * G + g) * 16 + c]);
-  } else if constexpr (MODE == ZERO_PACKED) {
-    const uint32_t word = ((const uint32_t*)Z)[((size_t)nt * G + g) * 2 + (c >> 3)];
-    return (float)((word >> (4 * (c & 7))) & 0xFu);
-  } else {
-    return (float)(1 << (BITS - 1));
-  }
+// Scale of group j from a scale record (interleaved with fp16 zero-points when Z16).
+template <bool Z16>
+__device__ inline float rec_scale(const uint32_t* w, int j) {
+  const uint32_t v = Z16 ? (w[j] & 0xFFFFu) : ((w[j / 2] >> (16 * (j % 2))) & 0xFFFFu);
+  return f16_to_f32((uint16_t)v);
+}
+// fp16 zero-point of group j from an interleaved record.
+__device__ inline float rec_zero16(const uint32_t* w, int j) { return f16_to_f32((uint16_t)(w[j] >> 16)); }
+// Packed zero-point of group j for column c from a packed-zero record.
+__device__ inline float rec_zero_packed(const uint32_t* w, int j, int c) {
+  return (float)((w[j] >> (4 * (c & 7))) & 0xFu);
 }
 
 }  // namespace wq

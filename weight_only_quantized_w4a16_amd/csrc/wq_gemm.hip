@@ -31,7 +31,7 @@ struct GemmArgs {
   const void* Z;
   const uint16_t* lut;
   uint16_t* y;
-  int M, N, K, G, gsz, ktiles, ntiles, mtiles, ntiles_wg;
+  int M, N, K, nrec, upr, ktiles, ntiles, mtiles, ntiles_wg;  // upr: 128-row units per metadata record
 };
 
 template <int DT, int BITS, int MODE, int GPU, bool EPI_SCALE, int BM>
@@ -67,6 +67,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs a) {
     fill_pair_table<BITS, false>(table, a.lut, tid, 256);
   }
   const uint32_t* tab = table + (lane & 31);
+  const DecodeConsts dk = make_decode_consts<DT>();
 
   // ---- activation staging: thread -> (row, chunk) slots of the BM x 128 tile
   u32x4 areg[A_LOADS];
@@ -90,10 +91,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs a) {
 
   // ---- weight words and their scales / zero-points (per wave, its NT column
   //      tiles) for one tile; column tiles past N are clamped (never stored)
-  constexpr int NG = UPT * GPU;       // scale groups per tile
+  constexpr bool Z16 = MODE == ZERO_F16;
+  constexpr int REC = (Z16 ? 4 : 2) * GPU;   // scale record bytes per column
+  constexpr int SW = REC < 4 ? 1 : REC / 4;  // words per scale record
+  constexpr int ZW = MODE == ZERO_PACKED ? GPU : 1;
   uint32_t bw[NT][WPL];
-  uint16_t sraw[NG][NT];
-  uint32_t zraw[NG][NT];
+  uint32_t srec[UPT][NT][SW];
+  uint32_t zrec[UPT][NT][ZW];
   auto b_load = [&](int kt) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -109,16 +113,21 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs a) {
     }
     if constexpr (!EPI_SCALE) {
 #pragma unroll
-      for (int j = 0; j < NG; ++j) {
-        const int g = (kt * KT + j * (128 / GPU)) / a.gsz;
+      for (int u = 0; u < UPT; ++u) {
+        const int rec = (kt * UPT + u) / a.upr;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           const int nt = min(nt0 + t, a.ntiles - 1);
-          const size_t mi = (size_t)nt * a.G + g;
-          sraw[j][t] = a.S[mi * 16 + c];
-          if constexpr (MODE == ZERO_F16) zraw[j][t] = ((const uint16_t*)a.Z)[mi * 16 + c];
-          else if constexpr (MODE == ZERO_PACKED) zraw[j][t] = ((const uint32_t*)a.Z)[mi * 2 + (c >> 3)];
-          else zraw[j][t] = 0u;
+          const size_t ri = (size_t)nt * a.nrec + rec;
+          const uint8_t* sp = (const uint8_t*)a.S + (ri * 16 + c) * REC;
+          if constexpr (REC == 2) srec[u][t][0] = *(const uint16_t*)sp;
+#pragma unroll
+          for (int w = 0; w < (REC == 2 ? 0 : SW); ++w) srec[u][t][w] = ((const uint32_t*)sp)[w];
+          if constexpr (MODE == ZERO_PACKED) {
+            const uint32_t* zp = (const uint32_t*)a.Z + (ri * 2 + (c >> 3)) * GPU;
+#pragma unroll
+            for (int w = 0; w < GPU; ++w) zrec[u][t][w] = zp[w];
+          }
         }
       }
     }
@@ -138,14 +147,19 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs a) {
 
   for (int kt = 0; kt < a.ktiles; ++kt) {
     uint32_t cw[NT][WPL];
-    uint16_t cs[NG][NT];
-    uint32_t cz[NG][NT];
+    uint32_t cs[UPT][NT][SW];
+    uint32_t cz[UPT][NT][ZW];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
 #pragma unroll
       for (int j = 0; j < WPL; ++j) cw[t][j] = bw[t][j];
 #pragma unroll
-      for (int j = 0; j < NG; ++j) { cs[j][t] = sraw[j][t]; cz[j][t] = zraw[j][t]; }
+      for (int u = 0; u < UPT; ++u) {
+#pragma unroll
+        for (int w = 0; w < SW; ++w) cs[u][t][w] = srec[u][t][w];
+#pragma unroll
+        for (int w = 0; w < ZW; ++w) cz[u][t][w] = zrec[u][t][w];
+      }
     }
     if (kt + 1 < a.ktiles) b_load(kt + 1);
 
@@ -157,15 +171,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs a) {
 
       sfor<GPU>([&](auto gc) {
         constexpr int gi = decltype(gc)::value;
-        constexpr int j = u * GPU + gi;
         ExactParams prm[NT];
         if constexpr (!EPI_SCALE) {
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
-            const float s = f16_to_f32(cs[j][t]);
+            const float s = rec_scale<Z16>(cs[u][t], gi);
             float z;
-            if constexpr (MODE == ZERO_F16) z = f16_to_f32((uint16_t)cz[j][t]);
-            else if constexpr (MODE == ZERO_PACKED) z = (float)((cz[j][t] >> (4 * (c & 7))) & 0xFu);
+            if constexpr (MODE == ZERO_F16) z = rec_zero16(cs[u][t], gi);
+            else if constexpr (MODE == ZERO_PACKED) z = rec_zero_packed(cz[u][t], gi, c);
             else z = (float)(1 << (BITS - 1));
             prm[t].s = s;
             prm[t].s_h = h2s(s);
@@ -179,9 +192,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs a) {
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
             if constexpr (EPI_SCALE)
-              bf[t] = offset_frag<BITS, DT, kb>(cw[t]);
+              bf[t] = offset_frag<BITS, DT, kb>(cw[t], dk);
             else
-              bf[t] = exact_frag<BITS, DT, MODE, kb>(cw[t], prm[t], tab);
+              bf[t] = exact_frag<BITS, DT, MODE, kb>(cw[t], prm[t], tab, dk);
           }
 #pragma unroll
           for (int i = 0; i < MT; ++i) {
@@ -208,7 +221,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs a) {
     if (nt0 + t >= a.ntiles) continue;
     const int n = (nt0 + t) * 16 + c;
     float s = 1.0f;
-    if constexpr (EPI_SCALE) s = load_scale(a.S, a.G, nt0 + t, 0, c);
+    if constexpr (EPI_SCALE) s = f16_to_f32(a.S[(size_t)(nt0 + t) * 16 + c]);  // one record per column tile
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
 #pragma unroll
@@ -249,7 +262,8 @@ wq_status WQ_CAT(launch_gemm_, WQ_VARIANT)(const ProductArgs& p) {
   g.Z = (const uint8_t*)p.packed + L.zeros_off;
   g.lut = p.lut;
   g.y = (uint16_t*)p.y;
-  g.M = p.M; g.N = p.N; g.K = p.K; g.G = L.G; g.gsz = L.gsz; g.ktiles = L.ktiles; g.ntiles = L.ntiles;
+  g.M = p.M; g.N = p.N; g.K = p.K; g.nrec = L.nrec; g.upr = (L.gsz > 128 ? L.gsz : 128) / 128;
+  g.ktiles = L.ktiles; g.ntiles = L.ntiles;
   g.mtiles = 0; g.ntiles_wg = 0;
   const int gpu = L.gsz >= 128 ? 1 : 128 / L.gsz;
   const bool epi = L.G == 1 && p.mode == SYM && D == F16;

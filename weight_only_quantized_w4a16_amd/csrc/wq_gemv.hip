@@ -6,15 +6,19 @@
 // reply).  So this kernel is built around one stream of the packed weight:
 //
 //  * A workgroup owns TN column tiles (16 columns each) and the whole of K;
-//    its WAVES waves split K and each streams its k-range of those tiles, PF
-//    tiles ahead (128-bit coalesced loads, 1 KiB per wave per tile).
+//    its waves (1..16, about 16 per CU over the grid) split K and each streams
+//    its k-range of those tiles PF tiles ahead with 128-bit coalesced buffer
+//    loads, 1 KiB per wave per tile.  Loads past the range are issued with an
+//    out-of-range offset instead of a branch, so the code stays straight-line
+//    and every wait on the memory counter is exact.
 //  * Codes become MFMA B operands in registers (offset or table decode);
 //    16x16x32 MFMAs do the multiply-accumulate, which leaves the vector ALUs
 //    to the decode.
 //  * Scales are applied after the MFMA, per 128-row unit of K, in fp32:
-//    sum_k x*s*(q - z) = s*(sum_k x*B - c*sum_k x) with B the decoded operand
-//    and c the zero-point correction; sum_k x comes from one more MFMA against
-//    a B of ones.  No per-element scaling and no zero subtraction in fp16.
+//    sum_k x*s*(q - z) = s*(sum_k x*B - c*sum_k x) with B = bias + q the
+//    decoded operand and c = bias + z; sum_k x comes from one more MFMA
+//    against a B of ones.  No per-element float work at all: the products
+//    x*B are exact in fp32 and the bias cancels in the correction.
 //  * M <= 4 packs (row m, k-block kb) into MFMA row 4m + kb, so one 128-bit
 //    activation load feeds the 4 k-blocks of a unit; larger M uses one MFMA
 //    row per activation row and one activation load per k-block.
@@ -35,56 +39,122 @@ struct GemvArgs {
   const void* Z;          // zero-points (re-laid) or null
   const uint16_t* lut;    // fp16 [2^bits] (table mode)
   uint16_t* y;            // [M][N]
-  int M, N, K, G, gsz, ktiles, kt_per_wave;
+  uint32_t codes_bytes, s_bytes, z_bytes;
+  int M, N, K, nrec, upr, ktiles, waves, kt_per_wave;  // upr: 128-row units per metadata record
 };
 
 // Decode k-block KB of a tile into a B operand.
 template <int BITS, int DT, int MODE, int KB>
-__device__ inline u32x4 decode_frag(const uint32_t* w, const uint32_t* tab) {
+__device__ inline u32x4 decode_frag(const uint32_t* w, const uint32_t* tab, const DecodeConsts& k) {
   if constexpr (MODE == LUT)
     return table_frag<BITS, KB>(w, tab);
   else
-    return offset_frag<BITS, DT, KB>(w);
+    return biased_frag<BITS, KB>(w, k);
 }
 
-// Zero-point correction c for (group, column): B - c == q - z (see offset_frag).
-template <int DT, int MODE, int BITS>
+// Zero-point correction c for (group, column): B - c == q - z (see biased_frag).
+template <int DT>
 __device__ inline float zero_corr(float z) {
-  if constexpr (DT == F16) return z - (float)(1 << (BITS - 1));
-  else return z + 128.0f;
+  return z + (DT == F16 ? 1024.0f : 128.0f);
 }
 
-template <int DT, int BITS, int MODE, int TN, int GPU, bool PACKED, int WAVES, int PF>
-__global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const GemvArgs a) {
+// Waves per workgroup are chosen at launch (1..16); the bound below lets 16.
+template <int DT, int BITS, int MODE, int TN, int GPU, bool PACKED, int PF>
+__global__ __launch_bounds__(1024) void gemv_kernel(const GemvArgs a) {
   constexpr int KT = BITS == 2 ? 256 : 128;
   constexpr int UPT = KT / 128;                 // 128-row units per tile
   constexpr int WPL = BITS == 3 ? 3 : 4;
   constexpr int NXA = PACKED ? UPT : 4 * UPT;   // activation loads per tile
-  constexpr int NS = UPT * GPU;                 // (scale, zero) pairs per tile per column tile
   constexpr int KBPG = 4 / GPU;                 // k-blocks per group inside a unit
   constexpr bool TABLE = MODE == LUT;
+  constexpr bool Z16 = MODE == ZERO_F16;
   constexpr bool HAS_Z = MODE == ZERO_F16 || MODE == ZERO_PACKED;
-  constexpr bool XS = HAS_Z || (DT == BF16 && MODE != LUT);
+  constexpr int REC = (Z16 ? 4 : 2) * GPU;      // scale record bytes per column
+  constexpr int SW = REC < 4 ? 1 : REC / 4;     // words per scale record
+  constexpr int ZREC = 4 * GPU;                 // packed-zero record bytes per column half
+  constexpr bool XS = MODE != LUT;              // uniform modes remove bias + z via row sums
   constexpr int NRED = PACKED ? 1 : 4;          // reduced values per lane per column tile
 
   __shared__ uint32_t table[TABLE ? (32 << (2 * BITS)) : 1];
-  __shared__ float red[WAVES][TN][NRED][64];
+  extern __shared__ float red[];                // [waves][TN][NRED][64]
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar arithmetic
   const int c = lane & 15, h = lane >> 4;
   const int nt0 = blockIdx.x * TN;
 
+  const rsrc_t rc = make_rsrc(a.codes, a.codes_bytes);
+  const rsrc_t rx = make_rsrc(a.x, (uint32_t)a.M * a.K * 2);
+  const rsrc_t rs = make_rsrc(a.S, a.s_bytes);
+  const rsrc_t rz = make_rsrc(HAS_Z ? a.Z : a.S, HAS_Z ? a.z_bytes : 0u);
+
+  // Buffer offsets = per-lane vector part + per-tile scalar part.  The vector
+  // part becomes kOutOfRange for loads that must return zero (rows past M,
+  // tiles past the wave's range).
+  //   packed:   lane c -> (m = c / 4, k-block c % 4) ; standard: lane c -> m = c
+  const int xm = PACKED ? (c >> 2) : c;
+  const uint32_t x_lane = xm < a.M ? (uint32_t)(xm * a.K + 8 * h + (PACKED ? 32 * (c & 3) : 0)) * 2u : kOutOfRange;
+  const uint32_t w_lane = (uint32_t)lane * WPL * 4;
+  const uint32_t s_lane = (uint32_t)c * REC;
+  const uint32_t zp_lane = (uint32_t)(c >> 3) * ZREC;
+
+  const int kt0 = wave * a.kt_per_wave;
+  const int kt1 = min(kt0 + a.kt_per_wave, a.ktiles);
+
+  struct Frame {
+    uint32_t w[TN][WPL];
+    u32x4 xa[NXA];
+    uint32_t s[TN][UPT][SW];                  // scale record (with fp16 zero-points when Z16)
+    uint32_t z[TN][UPT][HAS_Z && !Z16 ? GPU : 1];  // packed-zero record
+  };
+
+  // Loads of tile kt (all of them out of range, hence free, when kt >= kt1).
+  auto load = [&](Frame& f, int kt) {
+    const bool ok = kt < kt1;
+    const int ktc = ok ? kt : kt0;  // keeps the scalar offsets in range
+#pragma unroll
+    for (int t = 0; t < TN; ++t) {
+      const uint32_t so = (uint32_t)(((nt0 + t) * a.ktiles + ktc) * 64 * WPL * 4);
+      const uint32_t vo = ok ? w_lane : kOutOfRange;
+      if constexpr (WPL == 4) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rc, vo, so, kNontemporal);
+        f.w[t][0] = v[0]; f.w[t][1] = v[1]; f.w[t][2] = v[2]; f.w[t][3] = v[3];
+      } else {
+        typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+        const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(rc, vo, so, kNontemporal);
+        f.w[t][0] = v[0]; f.w[t][1] = v[1]; f.w[t][2] = v[2];
+      }
+    }
+    const uint32_t xv = ok ? x_lane : kOutOfRange;
+#pragma unroll
+    for (int i = 0; i < NXA; ++i) {
+      // packed: unit i covers rows 128 i ..; standard: k-block i covers rows 32 i ..
+      const uint32_t koff = (uint32_t)(ktc * KT + (PACKED ? 128 * i : 32 * i)) * 2u;
+      f.xa[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, xv, koff, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      const int rec = (ktc * UPT + u) / a.upr;
+#pragma unroll
+      for (int t = 0; t < TN; ++t) {
+        const uint32_t ri = (uint32_t)((nt0 + t) * a.nrec + rec);
+        load_record<REC>(rs, ok ? s_lane : kOutOfRange, ri * 16 * REC, f.s[t][u]);
+        if constexpr (MODE == ZERO_PACKED)
+          load_record<ZREC>(rz, ok ? zp_lane : kOutOfRange, ri * 2 * ZREC, f.z[t][u]);
+      }
+    }
+  };
+
+  Frame fr[PF];
+#pragma unroll
+  for (int p = 0; p < PF; ++p) load(fr[p], kt0 + p);
+
   if constexpr (TABLE) {
-    fill_pair_table<BITS, DT == BF16>(table, a.lut, threadIdx.x, WAVES * 64);
+    fill_pair_table<BITS, DT == BF16>(table, a.lut, threadIdx.x, a.waves * 64);
     __syncthreads();
   }
   const uint32_t* tab = table + (lane & 31);
-
-  // Activation row this lane feeds into the MFMA A operand.
-  //   packed:   lane c -> (m = c / 4, k-block c % 4) ; standard: lane c -> m = c
-  const int xm = PACKED ? (c >> 2) : c;
-  const bool xok = xm < a.M;
-  const uint16_t* xrow = a.x + (size_t)(xok ? xm : 0) * a.K + 8 * h + (PACKED ? 32 * (c & 3) : 0);
+  const DecodeConsts dk = make_decode_consts<DT>();
 
   float tot[TN][4];
 #pragma unroll
@@ -92,48 +162,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const GemvArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) tot[t][e] = 0.0f;
 
-  struct Frame {
-    uint32_t w[TN][WPL];
-    u32x4 xa[NXA];
-    uint16_t s[TN][NS];
-    uint32_t z[TN][NS];
-  };
-
-  auto load = [&](Frame& f, int kt) {
-#pragma unroll
-    for (int t = 0; t < TN; ++t) {
-      const uint32_t* p = a.codes + (((size_t)(nt0 + t) * a.ktiles + kt) * 64 + lane) * WPL;
-      if constexpr (WPL == 4) {
-        const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
-        f.w[t][0] = v[0]; f.w[t][1] = v[1]; f.w[t][2] = v[2]; f.w[t][3] = v[3];
-      } else {
-#pragma unroll
-        for (int j = 0; j < WPL; ++j) f.w[t][j] = __builtin_nontemporal_load(p + j);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < NXA; ++i) {
-      // packed: unit i covers rows 128 i ..; standard: k-block i covers rows 32 i ..
-      const int off = kt * KT + (PACKED ? 128 * i : 32 * i);
-      f.xa[i] = xok ? *(const u32x4*)(xrow + off) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      const int g = (kt * KT + j * (128 / GPU)) / a.gsz;
-#pragma unroll
-      for (int t = 0; t < TN; ++t) {
-        const size_t mi = ((size_t)(nt0 + t) * a.G + g);
-        f.s[t][j] = a.S[mi * 16 + c];
-        if constexpr (MODE == ZERO_F16) f.z[t][j] = ((const uint16_t*)a.Z)[mi * 16 + c];
-        else if constexpr (MODE == ZERO_PACKED) f.z[t][j] = ((const uint32_t*)a.Z)[mi * 2 + (c >> 3)];
-        else f.z[t][j] = 0u;
-      }
-    }
-  };
-
-  auto zero_of = [&](uint32_t zraw) -> float {
-    if constexpr (MODE == ZERO_F16) return f16_to_f32((uint16_t)zraw);
-    else if constexpr (MODE == ZERO_PACKED) return (float)((zraw >> (4 * (c & 7))) & 0xFu);
+  // zero-point of group j of unit u of column tile t
+  auto zero_of = [&](const Frame& f, int t, int u, int j) -> float {
+    if constexpr (MODE == ZERO_F16) return rec_zero16(f.s[t][u], j);
+    else if constexpr (MODE == ZERO_PACKED) return rec_zero_packed(f.z[t][u], j, c);
     else return (float)(1 << (BITS - 1));
   };
 
@@ -148,7 +180,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const GemvArgs a) {
           constexpr int kb = decltype(kbc)::value;
 #pragma unroll
           for (int t = 0; t < TN; ++t) {
-            const u32x4 b = decode_frag<BITS, DT, MODE, 4 * u + kb>(f.w[t], tab);
+            const u32x4 b = decode_frag<BITS, DT, MODE, 4 * u + kb>(f.w[t], tab, dk);
             acc[t][kb] = mfma16<DT>(f.xa[u], b, zero4);
           }
         });
@@ -159,10 +191,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const GemvArgs a) {
         for (int t = 0; t < TN; ++t) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int j = u * GPU + e / KBPG;
-            const float s = f16_to_f32(f.s[t][j]);
+            const int j = e / KBPG;
+            const float s = rec_scale<Z16>(f.s[t][u], j);
             float v = acc[t][e][e];
-            if constexpr (XS) v = __builtin_fmaf(-zero_corr<DT, MODE, BITS>(zero_of(f.z[t][j])), xs[e], v);
+            if constexpr (XS) v = __builtin_fmaf(-zero_corr<DT>(zero_of(f, t, u, j)), xs[e], v);
             tot[t][e] = __builtin_fmaf(s, v, tot[t][e]);
           }
         }
@@ -177,16 +209,15 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const GemvArgs a) {
             constexpr int kb = 4 * u + gi * KBPG + decltype(kc)::value;  // k-block inside the tile
 #pragma unroll
             for (int t = 0; t < TN; ++t) {
-              const u32x4 b = decode_frag<BITS, DT, MODE, kb>(f.w[t], tab);
+              const u32x4 b = decode_frag<BITS, DT, MODE, kb>(f.w[t], tab, dk);
               acc[t] = mfma16<DT>(f.xa[kb], b, acc[t]);
             }
             if constexpr (XS) xs = mfma16<DT>(f.xa[kb], ones_frag<DT>(), xs);
           });
-          const int j = u * GPU + gi;
 #pragma unroll
           for (int t = 0; t < TN; ++t) {
-            const float s = f16_to_f32(f.s[t][j]);
-            const float cz = XS ? zero_corr<DT, MODE, BITS>(zero_of(f.z[t][j])) : 0.0f;
+            const float s = rec_scale<Z16>(f.s[t][u], gi);
+            const float cz = XS ? zero_corr<DT>(zero_of(f, t, u, gi)) : 0.0f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               float v = acc[t][e];
@@ -199,42 +230,42 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const GemvArgs a) {
     });
   };
 
-  // Stream this wave's k-range, PF tiles ahead.
-  const int kt0 = wave * a.kt_per_wave;
-  const int kt1 = min(kt0 + a.kt_per_wave, a.ktiles);
-  if (kt0 < kt1) {
-    Frame fr[PF];
+  // Stream this wave's k-range PF tiles ahead.  Inside the loop every frame is
+  // a valid tile and every load unconditional (the last group's loads past the
+  // range are out of range and free); the last group is computed after it.
+  const int niter = kt1 > kt0 ? (kt1 - kt0 + PF - 1) / PF : 0;
+  for (int it = 0; it + 1 < niter; ++it) {
+    const int kt = kt0 + it * PF;
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+      compute(fr[p]);
+      load(fr[p], kt + p + PF);
+    }
+  }
+  if (niter > 0) {
+    const int kt = kt0 + (niter - 1) * PF;
 #pragma unroll
     for (int p = 0; p < PF; ++p)
-      if (kt0 + p < kt1) load(fr[p], kt0 + p);
-    for (int kt = kt0; kt < kt1; kt += PF) {
-#pragma unroll
-      for (int p = 0; p < PF; ++p) {
-        if (kt + p < kt1) {
-          compute(fr[p]);
-          if (kt + p + PF < kt1) load(fr[p], kt + p + PF);
-        }
-      }
-    }
+      if (kt + p < kt1) compute(fr[p]);
   }
 
   // Cross-wave reduction and store.
 #pragma unroll
   for (int t = 0; t < TN; ++t) {
+    float* r = red + ((size_t)(wave * TN + t) * NRED) * 64;
     if constexpr (PACKED) {
-      red[wave][t][0][lane] = (tot[t][0] + tot[t][1]) + (tot[t][2] + tot[t][3]);
+      r[lane] = (tot[t][0] + tot[t][1]) + (tot[t][2] + tot[t][3]);
     } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) red[wave][t][e][lane] = tot[t][e];
+      for (int e = 0; e < 4; ++e) r[e * 64 + lane] = tot[t][e];
     }
   }
   __syncthreads();
   constexpr int SLOTS = TN * NRED * 64;
-  for (int i = threadIdx.x; i < SLOTS; i += WAVES * 64) {
+  for (int i = threadIdx.x; i < SLOTS; i += a.waves * 64) {
     const int l = i & 63, e = (i >> 6) % NRED, t = i / (64 * NRED);
     float v = 0.0f;
-#pragma unroll
-    for (int w = 0; w < WAVES; ++w) v += red[w][t][e][l];
+    for (int w = 0; w < a.waves; ++w) v += red[((size_t)(w * TN + t) * NRED + e) * 64 + l];
     // packed: lane l = 16 m + col ; standard: row 4 (l / 16) + e, col l % 16
     const int m = PACKED ? (l >> 4) : 4 * (l >> 4) + e;
     const int n = (nt0 + t) * 16 + (l & 15);
@@ -245,34 +276,49 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(const GemvArgs a) {
 // ---------------------------------------------------------------------------
 // Launch-shape choice and dispatch.
 // ---------------------------------------------------------------------------
-template <int DT, int BITS, int MODE, int TN, int GPU, bool PACKED, int WAVES>
-wq_status run(const GemvArgs& g, int grid, hipStream_t s) {
-  constexpr int PF = (!PACKED && TN >= 2) ? 2 : 3;
-  hipLaunchKernelGGL((gemv_kernel<DT, BITS, MODE, TN, GPU, PACKED, WAVES, PF>), dim3(grid), dim3(WAVES * 64), 0, s,
-                     g);
+template <int DT, int BITS, int MODE, int TN, int GPU, bool PACKED, int PF>
+wq_status run(GemvArgs g, int grid, hipStream_t s) {
+  constexpr int NRED = PACKED ? 1 : 4;
+  const size_t lds = (size_t)g.waves * TN * NRED * 64 * sizeof(float);
+  hipLaunchKernelGGL((gemv_kernel<DT, BITS, MODE, TN, GPU, PACKED, PF>), dim3(grid), dim3(g.waves * 64), lds, s, g);
   return launch_status();
 }
 
+// Launch shape (measured on MI355X for the decode layer shapes): about 3072
+// waves over the grid, each streaming an equal share of K; the prefetch depth
+// grows with the tiles a wave streams (deeper prefetch costs registers and
+// out-of-range tail loads, so short ranges keep it at 2).
+inline int pick_waves(int grid, int ktiles, int tn) {
+  int w = 1;
+  while (w < 16 && (long)grid * w < 3072L && 2 * w <= ktiles && 2 * w * tn <= 16) w *= 2;
+  return w;
+}
+
+template <int DT, int BITS, int MODE, int TN, int GPU, bool PACKED>
+wq_status run_pf(GemvArgs g, int grid, hipStream_t s) {
+  const int tpw = g.kt_per_wave;
+  if (PACKED && tpw >= 8) return run<DT, BITS, MODE, TN, GPU, PACKED, 4>(g, grid, s);
+  if (PACKED && tpw >= 5) return run<DT, BITS, MODE, TN, GPU, PACKED, 3>(g, grid, s);
+  return run<DT, BITS, MODE, TN, GPU, PACKED, 2>(g, grid, s);
+}
+
 template <int DT, int BITS, int MODE, int GPU>
-wq_status pick_shape(const GemvArgs& g, hipStream_t s) {
+wq_status pick_shape(GemvArgs g, hipStream_t s) {
   const int ntiles = g.N / 16;
-  GemvArgs a = g;
   if (g.M <= 4) {
-    // Packed activations, one column tile per workgroup; small layers get
-    // 16 waves per workgroup so that every CU has enough loads in flight.
     const int grid = ntiles;
-    const int waves = (grid < 512 && g.ktiles >= 16) ? 16 : 4;
-    a.kt_per_wave = (g.ktiles + waves - 1) / waves;
-    if (waves == 16) return run<DT, BITS, MODE, 1, GPU, true, 16>(a, grid, s);
-    return run<DT, BITS, MODE, 1, GPU, true, 4>(a, grid, s);
+    g.waves = pick_waves(grid, g.ktiles, 1);
+    g.kt_per_wave = (g.ktiles + g.waves - 1) / g.waves;
+    return run_pf<DT, BITS, MODE, 1, GPU, true>(g, grid, s);
   }
   // One activation row per MFMA row; two column tiles per workgroup share the
   // activation loads when the grid stays large enough.
-  const int tn = (ntiles % 2 == 0 && ntiles / 2 >= 512) ? 2 : 1;
+  const int tn = (ntiles % 2 == 0 && ntiles / 2 >= 1024) ? 2 : 1;
   const int grid = ntiles / tn;
-  a.kt_per_wave = (g.ktiles + 7) / 8;
-  if (tn == 2) return run<DT, BITS, MODE, 2, GPU, false, 8>(a, grid, s);
-  return run<DT, BITS, MODE, 1, GPU, false, 8>(a, grid, s);
+  g.waves = pick_waves(grid, g.ktiles, tn);
+  g.kt_per_wave = (g.ktiles + g.waves - 1) / g.waves;
+  if (tn == 2) return run_pf<DT, BITS, MODE, 2, GPU, false>(g, grid, s);
+  return run_pf<DT, BITS, MODE, 1, GPU, false>(g, grid, s);
 }
 
 }  // namespace
@@ -288,7 +334,12 @@ wq_status WQ_CAT(launch_gemv_, WQ_VARIANT)(const ProductArgs& p) {
   g.Z = (const uint8_t*)p.packed + L.zeros_off;
   g.lut = p.lut;
   g.y = (uint16_t*)p.y;
-  g.M = p.M; g.N = p.N; g.K = p.K; g.G = L.G; g.gsz = L.gsz; g.ktiles = L.ktiles; g.kt_per_wave = 0;
+  g.codes_bytes = (uint32_t)L.codes_bytes;
+  g.s_bytes = (uint32_t)L.scales_bytes;
+  g.z_bytes = (uint32_t)L.zeros_bytes;
+  g.M = p.M; g.N = p.N; g.K = p.K; g.nrec = L.nrec; g.upr = (L.gsz > 128 ? L.gsz : 128) / 128;
+  g.ktiles = L.ktiles;
+  g.waves = 1; g.kt_per_wave = 0;
   const int gpu = L.gsz >= 128 ? 1 : 128 / L.gsz;  // groups per 128-row unit
   wq_status st = WQ_EINVAL;
   sfor<4>([&](auto mi) {

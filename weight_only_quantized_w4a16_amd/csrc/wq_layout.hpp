@@ -25,9 +25,17 @@
 //                  (lo = even element); pairs 0..14 at bits 6*(p%5) of word
 //                  p/5, pair 15 split over bits 30..31 of words 0, 1, 2.
 //
-// Scales / zero-points.  Re-laid column-tile major: fp16 [N/16][G][16]; fp16
-// zero-points the same; packed zero-points as 16 nibbles (one per column of
-// the tile, whatever the code width) in two words: uint32 [N/16][G][2].
+// Scales / zero-points.  Re-laid so that one vector load per 128-row unit of K
+// brings a lane everything it needs for its column.  With GPU = groups per
+// unit (1 for groups of 128 rows or more, else 128 / group_size) and a record
+// per (column tile, unit or group, column):
+//   scale records   fp16 [N/16][R][16][GPU]          R = K / max(group, 128)
+//                   or, with fp16 zero-points, (scale, zero) fp16 pairs
+//                   [N/16][R][16][GPU][2] (one record holds both);
+//   packed zeros    uint32 [N/16][R][2][GPU]: word j of half h holds the
+//                   zero-points of columns 8h..8h+7 of group j as nibbles
+//                   (whatever the code width).
+// Record r covers unit r when groups are smaller than 128 rows, else group r.
 #pragma once
 #include <stddef.h>
 #include <stdint.h>
@@ -44,10 +52,17 @@ WQ_HD int words_per_lane(int bits) { return bits == 3 ? 3 : 4; }
 WQ_HD int tile_bytes(int bits) { return 256 * words_per_lane(bits); }
 WQ_HD int kblocks_per_tile(int bits) { return tile_k(bits) / 32; }
 
+WQ_HD int groups_per_unit(int gsz) { return gsz >= 128 ? 1 : 128 / gsz; }
+// Metadata record of the 128-row unit `unit` (see above).
+WQ_HD int meta_record(int unit, int gsz) { return (unit * 128) / (gsz > 128 ? gsz : 128); }
+
 struct Layout {
   int K, N, bits, group_size, mode;
   int G;        // number of groups
   int gsz;      // rows per group (K for group_size == -1)
+  int gpu;      // groups per 128-row unit
+  int nrec;     // metadata records per column tile
+  int rec_bytes;  // scale record bytes per column: 2*gpu, or 4*gpu with fp16 zero-points
   int ktiles;   // K / tile_k
   int ntiles;   // N / 16
   size_t codes_off, codes_bytes;
@@ -64,16 +79,17 @@ inline Layout make_layout(int K, int N, int bits, int group_size, int mode) {
   L.K = K; L.N = N; L.bits = bits; L.group_size = group_size; L.mode = mode;
   L.gsz = group_size == -1 ? K : group_size;
   L.G = K / L.gsz;
+  L.gpu = groups_per_unit(L.gsz);
+  L.nrec = K / (L.gsz > 128 ? L.gsz : 128);
+  L.rec_bytes = (mode == ZERO_F16 ? 4 : 2) * L.gpu;
   L.ktiles = K / tile_k(bits);
   L.ntiles = N / 16;
   L.codes_off = 0;
   L.codes_bytes = (size_t)L.ntiles * L.ktiles * tile_bytes(bits);
   L.scales_off = align256(L.codes_bytes);
-  L.scales_bytes = (size_t)L.G * N * 2;
+  L.scales_bytes = (size_t)L.ntiles * L.nrec * 16 * L.rec_bytes;
   L.zeros_off = align256(L.scales_off + L.scales_bytes);
-  if (mode == ZERO_F16) L.zeros_bytes = (size_t)L.G * N * 2;
-  else if (mode == ZERO_PACKED) L.zeros_bytes = (size_t)L.G * L.ntiles * 8;
-  else L.zeros_bytes = 0;
+  L.zeros_bytes = mode == ZERO_PACKED ? (size_t)L.ntiles * L.nrec * 2 * L.gpu * 4 : 0;
   L.total = align256(L.zeros_off + L.zeros_bytes);
   return L;
 }
