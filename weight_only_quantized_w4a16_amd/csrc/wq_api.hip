@@ -314,6 +314,7 @@ static wq_status product(bool gemm, const void* x, wq_dtype dt, const void* pack
   if (mode == LUT && !lut) return WQ_EINVAL;
   if (((uintptr_t)x | (uintptr_t)y | (uintptr_t)packed) & 15) return WQ_EUNSUPPORTED;
   if (M > (1 << 24)) return WQ_EUNSUPPORTED;
+  if ((size_t)M * K * 2 >= ((size_t)1 << 31)) return WQ_EUNSUPPORTED;  // activation buffer offsets
   const size_t need = wq_workspace_bytes(M, N, K, bits, perm != nullptr);
   if (need && (!ws || ws_bytes < need)) return WQ_ENOSPACE;
   if (need && ((uintptr_t)ws & 15)) return WQ_EUNSUPPORTED;

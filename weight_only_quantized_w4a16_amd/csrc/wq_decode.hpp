@@ -42,6 +42,14 @@ __device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 }
 constexpr int kNontemporal = 2;  // cache policy of the streamed weight loads
 
+// 16 bytes per lane from a buffer straight into LDS: lane L writes
+// lds[L] (the wave's 1 KiB lands contiguously from `lds`, which must be
+// wave-uniform).  A separate device function keeps the LDS address-space cast
+// out of kernel bodies, which the host compilation pass must still accept.
+__device__ inline void buffer_load_lds16(rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+
 __device__ inline uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
 __device__ inline h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
 __device__ inline h2 h2s(float a) { return h2{(_Float16)a, (_Float16)a}; }

@@ -4,10 +4,15 @@
 // the weights on the fly before the multiply, no slowdown with context
 // length).  On gfx950 the product runs on 16x16x32 MFMAs:
 //
-//  * workgroup tile BM x 128 (BM = 128 or 64), four waves in a 2 x 2 grid;
-//  * the activation tile (BM rows x 128 k) is staged through LDS, double
-//    buffered, 16-byte chunks XOR-swizzled by row so the MFMA A reads of 16
-//    rows hit 16 different bank groups;
+//  * workgroup tile BM x 256 (BM = 128, or 64 for small M), four waves side
+//    by side along N: each wave owns 64 columns for all BM rows, so every
+//    weight fragment is dequantised exactly once per workgroup and reused by
+//    BM / 16 MFMAs;
+//  * the activation tile (BM rows x 128 k) is staged through LDS by buffer
+//    loads that write LDS directly (no staging registers), double buffered;
+//    16-byte chunks are XOR-swizzled by row -- the swizzle is applied on the
+//    source side, since a wave's load lands contiguously -- so the MFMA A
+//    reads of 16 rows hit 16 different bank groups;
 //  * each wave loads the packed codes of its 64 columns straight from global
 //    memory -- the tile layout already is the MFMA B operand, one 128-bit load
 //    per lane per tile -- and dequantises them in registers with the exact
@@ -31,103 +36,115 @@ struct GemmArgs {
   const void* Z;
   const uint16_t* lut;
   uint16_t* y;
+  uint32_t codes_bytes, s_bytes, z_bytes;
   int M, N, K, nrec, upr, ktiles, ntiles, mtiles, ntiles_wg;  // upr: 128-row units per metadata record
 };
 
+// s_waitcnt immediate (gfx9 encoding) that waits until at most n vector
+// memory operations are outstanding and leaves the other counters alone.
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
 template <int DT, int BITS, int MODE, int GPU, bool EPI_SCALE, int BM>
-__global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs a) {
-  constexpr int BN = 128;
+__global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
+  constexpr int BN = 256;
   constexpr int KT = BITS == 2 ? 256 : 128;
   constexpr int UPT = KT / 128;
   constexpr int WPL = BITS == 3 ? 3 : 4;
-  constexpr int MT = BM / 32;         // 16-row subtiles per wave (wave covers BM/2 rows)
+  constexpr int MT = BM / 16;         // 16-row subtiles per wave (a wave covers all BM rows)
   constexpr int NT = 4;               // 16-column tiles per wave (64 columns)
   constexpr int KBPG = 4 / GPU;
   constexpr bool TABLE = MODE == LUT;
-  constexpr int AROW_CHUNKS = 16;     // 128 halves per LDS row = 16 chunks of 16 B
-  constexpr int A_LOADS = BM * AROW_CHUNKS / 256;  // 16-byte chunks per thread per unit
-
-  __shared__ uint32_t table[TABLE ? (32 << (2 * BITS)) : 1];
-  __shared__ u32x4 As[2][BM * AROW_CHUNKS];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int c = lane & 15, h = lane >> 4;
-  const int wm = wave >> 1, wn = wave & 1;
-
-  // Tile order: consecutive workgroups (which land on different XCDs) walk
-  // down M for one column block, so the weights of a column block are shared
-  // through the last-level cache while the activation rows stream.
-  const int bid = blockIdx.x;
-  const int mt = bid % a.mtiles, nb = bid / a.mtiles;
-  const int m0 = mt * BM;
-  const int nt0 = nb * (BN / 16) + wn * NT;  // first 16-column tile of this wave
-
-  if constexpr (TABLE) {
-    fill_pair_table<BITS, false>(table, a.lut, tid, 256);
-  }
-  const uint32_t* tab = table + (lane & 31);
-  const DecodeConsts dk = make_decode_consts<DT>();
-
-  // ---- activation staging: thread -> (row, chunk) slots of the BM x 128 tile
-  u32x4 areg[A_LOADS];
-  auto a_load = [&](int unit) {
-#pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) {
-      const int slot = tid + 256 * i;
-      const int r = slot >> 4, ch = slot & 15;
-      const int m = m0 + r;
-      areg[i] = m < a.M ? *(const u32x4*)(a.x + (size_t)m * a.K + unit * 128 + ch * 8) : u32x4{0u, 0u, 0u, 0u};
-    }
-  };
-  auto a_store = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) {
-      const int slot = tid + 256 * i;
-      const int r = slot >> 4, ch = slot & 15;
-      As[buf][r * AROW_CHUNKS + (ch ^ (r & 15))] = areg[i];
-    }
-  };
-
-  // ---- weight words and their scales / zero-points (per wave, its NT column
-  //      tiles) for one tile; column tiles past N are clamped (never stored)
   constexpr bool Z16 = MODE == ZERO_F16;
   constexpr int REC = (Z16 ? 4 : 2) * GPU;   // scale record bytes per column
   constexpr int SW = REC < 4 ? 1 : REC / 4;  // words per scale record
+  constexpr int ZREC = 4 * GPU;              // packed-zero record bytes per column half
   constexpr int ZW = MODE == ZERO_PACKED ? GPU : 1;
+  constexpr int AW = BM / 16;         // 1-KiB activation loads per wave per unit
+
+  __shared__ uint32_t table[TABLE ? (32 << (2 * BITS)) : 1];
+  // Two stages of the BM x 128 activation tile, 16-byte chunks, row r at
+  // chunk (c ^ (r % 16)).  Separate arrays so each stage's reads and loads are
+  // distinct objects.
+  __shared__ __attribute__((aligned(16))) u32x4 As0[BM * 16];
+  __shared__ __attribute__((aligned(16))) u32x4 As1[BM * 16];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // -> 64-column slice
+  const int c = lane & 15, h = lane >> 4;
+
+  // Consecutive workgroups walk down M for one column block, so a column
+  // block's weights are shared through the caches while activation rows stream.
+  const int bid = blockIdx.x;
+  const int mt = bid % a.mtiles, nb = bid / a.mtiles;
+  const int m0 = mt * BM;
+  const int nt0 = nb * (BN / 16) + wave * NT;  // first 16-column tile of this wave
+
+  const rsrc_t rx = make_rsrc(a.x, (uint32_t)a.M * a.K * 2);
+  const rsrc_t rc = make_rsrc(a.codes, a.codes_bytes);
+  const rsrc_t rs = make_rsrc(a.S, a.s_bytes);
+  const rsrc_t rz = make_rsrc(MODE == ZERO_PACKED ? a.Z : a.S, MODE == ZERO_PACKED ? a.z_bytes : 0u);
+
+  if constexpr (TABLE) fill_pair_table<BITS, false>(table, a.lut, tid, 256);
+  const uint32_t* tab = table + (lane & 31);
+  const DecodeConsts dk = make_decode_consts<DT>();
+
+  // ---- activations: wave issues AW LDS-destination loads of 1 KiB per unit.
+  //      Load i of this wave fills rows 4j..4j+3 (j = wave + 4 i); lane L lands
+  //      at row 4j + L / 16, physical chunk L % 16, so it fetches logical chunk
+  //      (L % 16) ^ (row % 16).  Rows past M read as zero (out of range).
+  uint32_t a_voff[AW];
+#pragma unroll
+  for (int i = 0; i < AW; ++i) {
+    const int row = 4 * (wave + 4 * i) + (lane >> 4);
+    const int lc = (lane & 15) ^ (row & 15);
+    a_voff[i] = m0 + row < a.M ? (uint32_t)(((m0 + row) * a.K + 8 * lc) * 2) : kOutOfRange;
+  }
+  auto a_issue = [&](int unit, u32x4* stage) {
+#pragma unroll
+    for (int i = 0; i < AW; ++i)
+      buffer_load_lds16(rx, stage + (wave + 4 * i) * 64, a_voff[i], (uint32_t)unit * 256);
+  };
+
+  // ---- weight words and metadata records of one tile (out of range past K);
+  //      column tiles past N are clamped (never stored)
+  uint32_t b_voff[NT], s_soff_t[NT], z_soff_t[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int nt = min(nt0 + t, a.ntiles - 1);
+    b_voff[t] = (uint32_t)(nt * a.ktiles * 64 + lane) * WPL * 4;
+    s_soff_t[t] = (uint32_t)(nt * a.nrec) * 16 * REC;
+    z_soff_t[t] = (uint32_t)(nt * a.nrec) * 2 * ZREC;
+  }
   uint32_t bw[NT][WPL];
   uint32_t srec[UPT][NT][SW];
   uint32_t zrec[UPT][NT][ZW];
   auto b_load = [&](int kt) {
+    const bool ok = kt < a.ktiles;
+    const int ktc = ok ? kt : 0;
+    const uint32_t kofs = (uint32_t)ktc * 64 * WPL * 4;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const int nt = min(nt0 + t, a.ntiles - 1);
-      const uint32_t* p = a.codes + (((size_t)nt * a.ktiles + kt) * 64 + lane) * WPL;
+      const uint32_t vo = ok ? b_voff[t] + kofs : kOutOfRange;
       if constexpr (WPL == 4) {
-        const u32x4 v = *(const u32x4*)p;
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rc, vo, 0, 0);
         bw[t][0] = v[0]; bw[t][1] = v[1]; bw[t][2] = v[2]; bw[t][3] = v[3];
       } else {
-#pragma unroll
-        for (int j = 0; j < WPL; ++j) bw[t][j] = p[j];
+        typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+        const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(rc, vo, 0, 0);
+        bw[t][0] = v[0]; bw[t][1] = v[1]; bw[t][2] = v[2];
       }
     }
     if constexpr (!EPI_SCALE) {
 #pragma unroll
       for (int u = 0; u < UPT; ++u) {
-        const int rec = (kt * UPT + u) / a.upr;
+        const uint32_t rec = (uint32_t)((ktc * UPT + u) / a.upr);
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-          const int nt = min(nt0 + t, a.ntiles - 1);
-          const size_t ri = (size_t)nt * a.nrec + rec;
-          const uint8_t* sp = (const uint8_t*)a.S + (ri * 16 + c) * REC;
-          if constexpr (REC == 2) srec[u][t][0] = *(const uint16_t*)sp;
-#pragma unroll
-          for (int w = 0; w < (REC == 2 ? 0 : SW); ++w) srec[u][t][w] = ((const uint32_t*)sp)[w];
-          if constexpr (MODE == ZERO_PACKED) {
-            const uint32_t* zp = (const uint32_t*)a.Z + (ri * 2 + (c >> 3)) * GPU;
-#pragma unroll
-            for (int w = 0; w < GPU; ++w) zrec[u][t][w] = zp[w];
-          }
+          load_record<REC>(rs, ok ? (uint32_t)c * REC : kOutOfRange, s_soff_t[t] + rec * 16 * REC, srec[u][t]);
+          if constexpr (MODE == ZERO_PACKED)
+            load_record<ZREC>(rz, ok ? (uint32_t)(c >> 3) * ZREC : kOutOfRange, z_soff_t[t] + rec * 2 * ZREC,
+                              zrec[u][t]);
         }
       }
     }
@@ -139,10 +156,52 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs a) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[i][t] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 
+  // One 128-row unit of K from stage `As`: 4 k-blocks of MT x NT MFMAs.
+  auto compute_unit = [&](const u32x4* As, const uint32_t (&cw)[NT][WPL], const uint32_t (&cs)[NT][SW],
+                          const uint32_t (&cz)[NT][ZW], auto uc) {
+    constexpr int u = decltype(uc)::value;
+    sfor<GPU>([&](auto gc) {
+      constexpr int gi = decltype(gc)::value;
+      ExactParams prm[NT];
+      if constexpr (!EPI_SCALE) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const float sv = rec_scale<Z16>(cs[t], gi);
+          float z;
+          if constexpr (MODE == ZERO_F16) z = rec_zero16(cs[t], gi);
+          else if constexpr (MODE == ZERO_PACKED) z = rec_zero_packed(cz[t], gi, c);
+          else z = (float)(1 << (BITS - 1));
+          prm[t].s = sv;
+          prm[t].s_h = h2s(sv);
+          prm[t].sz = MODE == LUT ? 0.0f : sv * z;
+        }
+      }
+      sfor<KBPG>([&](auto kc) {
+        constexpr int kbu = gi * KBPG + decltype(kc)::value;  // k-block inside the unit
+        constexpr int kb = 4 * u + kbu;                        // k-block inside the tile
+        u32x4 bf[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          if constexpr (EPI_SCALE)
+            bf[t] = offset_frag<BITS, DT, kb>(cw[t], dk);
+          else
+            bf[t] = exact_frag<BITS, DT, MODE, kb>(cw[t], prm[t], tab, dk);
+        }
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+          const int r = 16 * i + c;
+          const u32x4 af = As[r * 16 + ((4 * kbu + h) ^ (r & 15))];
+#pragma unroll
+          for (int t = 0; t < NT; ++t) acc[i][t] = mfma16<DT>(af, bf[t], acc[i][t]);
+        }
+      });
+    });
+  };
+
   const int nunits = a.ktiles * UPT;
-  a_load(0);
+  a_issue(0, As0);
   b_load(0);
-  a_store(0);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();
 
   for (int kt = 0; kt < a.ktiles; ++kt) {
@@ -161,55 +220,21 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs a) {
         for (int w = 0; w < ZW; ++w) cz[u][t][w] = zrec[u][t][w];
       }
     }
-    if (kt + 1 < a.ktiles) b_load(kt + 1);
-
     sfor<UPT>([&](auto uc) {
       constexpr int u = decltype(uc)::value;
       const int unit = kt * UPT + u;
-      const int buf = unit & 1;
-      if (unit + 1 < nunits) a_load(unit + 1);
-
-      sfor<GPU>([&](auto gc) {
-        constexpr int gi = decltype(gc)::value;
-        ExactParams prm[NT];
-        if constexpr (!EPI_SCALE) {
-#pragma unroll
-          for (int t = 0; t < NT; ++t) {
-            const float s = rec_scale<Z16>(cs[u][t], gi);
-            float z;
-            if constexpr (MODE == ZERO_F16) z = rec_zero16(cs[u][t], gi);
-            else if constexpr (MODE == ZERO_PACKED) z = rec_zero_packed(cz[u][t], gi, c);
-            else z = (float)(1 << (BITS - 1));
-            prm[t].s = s;
-            prm[t].s_h = h2s(s);
-            prm[t].sz = MODE == LUT ? 0.0f : s * z;
-          }
-        }
-        sfor<KBPG>([&](auto kc) {
-          constexpr int kbu = gi * KBPG + decltype(kc)::value;  // k-block inside the unit
-          constexpr int kb = 4 * u + kbu;                        // k-block inside the tile
-          u32x4 bf[NT];
-#pragma unroll
-          for (int t = 0; t < NT; ++t) {
-            if constexpr (EPI_SCALE)
-              bf[t] = offset_frag<BITS, DT, kb>(cw[t], dk);
-            else
-              bf[t] = exact_frag<BITS, DT, MODE, kb>(cw[t], prm[t], tab, dk);
-          }
-#pragma unroll
-          for (int i = 0; i < MT; ++i) {
-            const int r = wm * (BM / 2) + 16 * i + c;
-            const u32x4 af = As[buf][r * AROW_CHUNKS + ((4 * kbu + h) ^ (r & 15))];
-#pragma unroll
-            for (int t = 0; t < NT; ++t) acc[i][t] = mfma16<DT>(af, bf[t], acc[i][t]);
-          }
-        });
-      });
-
+      // the stage of a unit alternates; with UPT = 2 it follows u, else kt
+      const bool odd = UPT == 2 ? (u == 1) : (kt & 1);
+      // Next weights (once per tile), then the next unit's activations; both
+      // stream while this unit computes.  The wait counter logic does not
+      // see the LDS-destination loads, so the current weights were copied out
+      // before any of them was issued and the unit ends with an explicit full
+      // wait and a barrier.
+      if constexpr (u == 0) b_load(kt + 1);
+      if (unit + 1 < nunits) a_issue(unit + 1, odd ? As0 : As1);
+      compute_unit(odd ? As1 : As0, cw, cs[u], cz[u], uc);
       if (unit + 1 < nunits) {
-        // Buffer buf ^ 1 was last read in the previous unit, which every wave
-        // finished before the barrier that ended it.
-        a_store(buf ^ 1);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         __syncthreads();
       }
     });
@@ -226,7 +251,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmArgs a) {
     for (int i = 0; i < MT; ++i) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int m = m0 + wm * (BM / 2) + 16 * i + 4 * h + e;
+        const int m = m0 + 16 * i + 4 * h + e;
         if (m < a.M) {
           const float v = acc[i][t][e] * s;
           a.y[(size_t)m * a.N + n] = DT == F16 ? f32_to_f16(v) : f32_to_bf16(v);
@@ -240,7 +265,7 @@ template <int DT, int BITS, int MODE, int GPU, bool EPI>
 wq_status run_gemm(GemmArgs g, hipStream_t s) {
   const int bm = g.M <= 64 ? 64 : 128;
   g.mtiles = (g.M + bm - 1) / bm;
-  g.ntiles_wg = (g.N + 127) / 128;
+  g.ntiles_wg = (g.N + 255) / 256;
   const int grid = g.mtiles * g.ntiles_wg;
   if (bm == 64)
     hipLaunchKernelGGL((gemm_kernel<DT, BITS, MODE, GPU, EPI, 64>), dim3(grid), dim3(256), 0, s, g);
@@ -262,6 +287,9 @@ wq_status WQ_CAT(launch_gemm_, WQ_VARIANT)(const ProductArgs& p) {
   g.Z = (const uint8_t*)p.packed + L.zeros_off;
   g.lut = p.lut;
   g.y = (uint16_t*)p.y;
+  g.codes_bytes = (uint32_t)L.codes_bytes;
+  g.s_bytes = (uint32_t)L.scales_bytes;
+  g.z_bytes = (uint32_t)L.zeros_bytes;
   g.M = p.M; g.N = p.N; g.K = p.K; g.nrec = L.nrec; g.upr = (L.gsz > 128 ? L.gsz : 128) / 128;
   g.ktiles = L.ktiles; g.ntiles = L.ntiles;
   g.mtiles = 0; g.ntiles_wg = 0;
