@@ -19,7 +19,9 @@
 //    decode (RN(s*(q - z)) or RN(s*T[q]) in the activation dtype), so the
 //    product multiplies exactly the weights the debug dump writes;
 //  * with one scale per column and fp16 symmetric codes, the scale moves to
-//    the epilogue (the B operand is then the exact integer q - 8).
+//    the epilogue (the weight operand is then the exact integer q - 8);
+//  * the weights are the MFMA A operand and the activations B, so each lane
+//    ends with four consecutive outputs of one row: 8-byte stores.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -73,8 +75,11 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // -> 64-column slice
   const int c = lane & 15, h = lane >> 4;
 
-  // Consecutive workgroups walk down M for one column block, so a column
-  // block's weights are shared through the caches while activation rows stream.
+  // Tile order: M fastest.  Workgroups are dispatched to the 8 XCDs
+  // round-robin (id i -> XCD i % 8, each XCD with its own L2), so with a
+  // multiple of 8 row tiles an XCD only ever sees 1/8 of the activation row
+  // tiles (which stay in its L2) while the weight column blocks stream past,
+  // each shared by the XCD's workgroups on the same block.
   const int bid = blockIdx.x;
   const int mt = bid % a.mtiles, nb = bid / a.mtiles;
   const int m0 = mt * BM;
@@ -116,23 +121,31 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
     s_soff_t[t] = (uint32_t)(nt * a.nrec) * 16 * REC;
     z_soff_t[t] = (uint32_t)(nt * a.nrec) * 2 * ZREC;
   }
-  uint32_t bw[NT][WPL];
-  uint32_t srec[UPT][NT][SW];
-  uint32_t zrec[UPT][NT][ZW];
-  auto b_load = [&](int kt) {
+  // Weight registers of one tile.
+  struct BSet {
+    uint32_t w[NT][WPL];
+    uint32_t s[UPT][NT][SW];
+    uint32_t z[UPT][NT][ZW];
+  };
+  // loads issued by one b_load (codes, scale records, packed-zero records)
+  constexpr int NBL = NT * (1 + (EPI_SCALE ? 0 : UPT) + (MODE == ZERO_PACKED ? UPT : 0));
+  auto b_load = [&](BSet& bs, int kt) {
+    // Past K every offset gets 2^31 added (out of range, reads zero): a
+    // scalar add instead of a select, so the code stays branch-free.
     const bool ok = kt < a.ktiles;
     const int ktc = ok ? kt : 0;
-    const uint32_t kofs = (uint32_t)ktc * 64 * WPL * 4;
+    const uint32_t oob = ok ? 0u : kOutOfRange;
+    const uint32_t kofs = (uint32_t)ktc * 64 * WPL * 4 + oob;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const uint32_t vo = ok ? b_voff[t] + kofs : kOutOfRange;
+      const uint32_t vo = b_voff[t] + kofs;
       if constexpr (WPL == 4) {
         const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rc, vo, 0, 0);
-        bw[t][0] = v[0]; bw[t][1] = v[1]; bw[t][2] = v[2]; bw[t][3] = v[3];
+        bs.w[t][0] = v[0]; bs.w[t][1] = v[1]; bs.w[t][2] = v[2]; bs.w[t][3] = v[3];
       } else {
         typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
         const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(rc, vo, 0, 0);
-        bw[t][0] = v[0]; bw[t][1] = v[1]; bw[t][2] = v[2];
+        bs.w[t][0] = v[0]; bs.w[t][1] = v[1]; bs.w[t][2] = v[2];
       }
     }
     if constexpr (!EPI_SCALE) {
@@ -141,10 +154,9 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
         const uint32_t rec = (uint32_t)((ktc * UPT + u) / a.upr);
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-          load_record<REC>(rs, ok ? (uint32_t)c * REC : kOutOfRange, s_soff_t[t] + rec * 16 * REC, srec[u][t]);
+          load_record<REC>(rs, (uint32_t)c * REC + oob, s_soff_t[t] + rec * 16 * REC, bs.s[u][t]);
           if constexpr (MODE == ZERO_PACKED)
-            load_record<ZREC>(rz, ok ? (uint32_t)(c >> 3) * ZREC : kOutOfRange, z_soff_t[t] + rec * 2 * ZREC,
-                              zrec[u][t]);
+            load_record<ZREC>(rz, (uint32_t)(c >> 3) * ZREC + oob, z_soff_t[t] + rec * 2 * ZREC, bs.z[u][t]);
         }
       }
     }
@@ -192,70 +204,75 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
           const int r = 16 * i + c;
           const u32x4 af = As[r * 16 + ((4 * kbu + h) ^ (r & 15))];
 #pragma unroll
-          for (int t = 0; t < NT; ++t) acc[i][t] = mfma16<DT>(af, bf[t], acc[i][t]);
+          for (int t = 0; t < NT; ++t) acc[i][t] = mfma16<DT>(bf[t], af, acc[i][t]);
         }
       });
     });
   };
 
+  // Pipeline: weights are loaded two tiles ahead (two register sets, the
+  // tile loop unrolled by two), activations one 128-row unit ahead into the
+  // other LDS stage.  In each unit the activation loads are issued before the
+  // weight loads, so the unit can end by waiting only until the activation
+  // loads are done (at most NBL newer operations outstanding) while the next
+  // weights keep streaming.  The compiler's wait tracking does not see the
+  // LDS-destination loads, hence the explicit waits; a scheduling barrier
+  // keeps the two groups of loads in program order.
   const int nunits = a.ktiles * UPT;
+  BSet set0, set1;
   a_issue(0, As0);
-  b_load(0);
+  b_load(set0, 0);
+  b_load(set1, 1);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();
 
-  for (int kt = 0; kt < a.ktiles; ++kt) {
-    uint32_t cw[NT][WPL];
-    uint32_t cs[UPT][NT][SW];
-    uint32_t cz[UPT][NT][ZW];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-#pragma unroll
-      for (int j = 0; j < WPL; ++j) cw[t][j] = bw[t][j];
-#pragma unroll
-      for (int u = 0; u < UPT; ++u) {
-#pragma unroll
-        for (int w = 0; w < SW; ++w) cs[u][t][w] = srec[u][t][w];
-#pragma unroll
-        for (int w = 0; w < ZW; ++w) cz[u][t][w] = zrec[u][t][w];
-      }
-    }
+  auto tile = [&](int kt, BSet& cur) {
+    BSet use = cur;  // copied out before this set is reloaded
     sfor<UPT>([&](auto uc) {
       constexpr int u = decltype(uc)::value;
       const int unit = kt * UPT + u;
       // the stage of a unit alternates; with UPT = 2 it follows u, else kt
       const bool odd = UPT == 2 ? (u == 1) : (kt & 1);
-      // Next weights (once per tile), then the next unit's activations; both
-      // stream while this unit computes.  The wait counter logic does not
-      // see the LDS-destination loads, so the current weights were copied out
-      // before any of them was issued and the unit ends with an explicit full
-      // wait and a barrier.
-      if constexpr (u == 0) b_load(kt + 1);
       if (unit + 1 < nunits) a_issue(unit + 1, odd ? As0 : As1);
-      compute_unit(odd ? As1 : As0, cw, cs[u], cz[u], uc);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (u == 0) b_load(cur, kt + 2);
+      compute_unit(odd ? As1 : As0, use.w, use.s[u], use.z[u], uc);
       if (unit + 1 < nunits) {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        // u == 0: the weight loads issued after the activation loads may stay
+        // in flight; later units have no newer loads
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(u == 0 ? NBL : 0));
         __syncthreads();
       }
     });
+  };
+  for (int kt = 0; kt < a.ktiles; kt += 2) {
+    tile(kt, set0);
+    if (kt + 1 < a.ktiles) tile(kt + 1, set1);
   }
 
-  // ---- epilogue: lane holds rows 4h + e of each 16-row subtile, column c
+  // ---- epilogue.  The MFMAs take the weights as the A operand and the
+  //      activations as B, so they produce y transposed: lane (c, h) holds
+  //      row m0 + 16 i + c, columns 4h .. 4h + 3 of column tile t -- four
+  //      consecutive outputs, one 8-byte store.
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     if (nt0 + t >= a.ntiles) continue;
-    const int n = (nt0 + t) * 16 + c;
-    float s = 1.0f;
-    if constexpr (EPI_SCALE) s = f16_to_f32(a.S[(size_t)(nt0 + t) * 16 + c]);  // one record per column tile
+    const int n = (nt0 + t) * 16 + 4 * h;
+    float s[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+    if constexpr (EPI_SCALE) {  // one scale record per column tile
+      typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+      const u16x4 sv = *(const u16x4*)(a.S + (size_t)(nt0 + t) * 16 + 4 * h);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[e] = f16_to_f32(sv[e]);
+    }
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int m = m0 + 16 * i + 4 * h + e;
-        if (m < a.M) {
-          const float v = acc[i][t][e] * s;
-          a.y[(size_t)m * a.N + n] = DT == F16 ? f32_to_f16(v) : f32_to_bf16(v);
-        }
+      const int m = m0 + 16 * i + c;
+      if (m < a.M) {
+        const uint32_t lo = pack2<DT>(acc[i][t][0] * s[0], acc[i][t][1] * s[1]);
+        const uint32_t hi = pack2<DT>(acc[i][t][2] * s[2], acc[i][t][3] * s[3]);
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        *(u32x2*)(a.y + (size_t)m * a.N + n) = u32x2{lo, hi};
       }
     }
   }
@@ -263,9 +280,10 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
 
 template <int DT, int BITS, int MODE, int GPU, bool EPI>
 wq_status run_gemm(GemmArgs g, hipStream_t s) {
-  const int bm = g.M <= 64 ? 64 : 128;
-  g.mtiles = (g.M + bm - 1) / bm;
+  // 128-row tiles unless that leaves fewer than about two workgroups per CU
   g.ntiles_wg = (g.N + 255) / 256;
+  const int bm = (g.M <= 64 || (long)((g.M + 127) / 128) * g.ntiles_wg < 480) ? 64 : 128;
+  g.mtiles = (g.M + bm - 1) / bm;
   const int grid = g.mtiles * g.ntiles_wg;
   if (bm == 64)
     hipLaunchKernelGGL((gemm_kernel<DT, BITS, MODE, GPU, EPI, 64>), dim3(grid), dim3(256), 0, s, g);
