@@ -12,6 +12,7 @@ wq_oracle.c by oracle/build.py.  Every function mirrors a C entry point:
   unpack_zeros / pack_zeros   packed zero-points (per group row, a bit stream along N)
   dequant                     w = RN_dtype(s*(q-z)) or RN_dtype(s*T[q]), one rounding
   linear                      y = x . w in fp64, k ascending, optional column subset
+  swiglu / linear_gate_up     h = SiLU(x . W_gate) * (x . W_up) for fused gate+up weights
   decode / encode             exact fp16/bf16 -> fp64 and RNE fp64 -> fp16/bf16
 """
 import ctypes
@@ -53,6 +54,10 @@ def lib():
         L.wqo_f64_to_bf16.argtypes = [ctypes.c_double]
         L.wqo_f64_to_bf16.restype = ctypes.c_uint16
         L.wqo_num_threads.argtypes = []
+        L.wqo_silu.argtypes = [ctypes.c_double]
+        L.wqo_silu.restype = ctypes.c_double
+        L.wqo_swiglu.argtypes = [P, P, ctypes.c_size_t, P]
+        L.wqo_swiglu.restype = None
         _lib = L
     return _lib
 
@@ -143,6 +148,26 @@ def dequant(qweight, scales, zeros, mode, lut, g_idx, K, N, bits, group_size, dt
     _check(lib().wqo_dequant(_p(qweight), _p(scales), _p(z), mode, _p(lut), _p(g_idx),
                              K, N, bits, group_size, dtype, _p(out)))
     return out
+
+
+def swiglu(g, u):
+    """h = SiLU(g) * u elementwise (fp64)."""
+    g = _c(g, np.float64)
+    u = _c(u, np.float64)
+    assert g.shape == u.shape
+    h = np.empty(g.shape, np.float64)
+    lib().wqo_swiglu(_p(g), _p(u), g.size, _p(h))
+    return h
+
+
+def linear_gate_up(x, dtype, qweight, scales, zeros, mode, lut, g_idx, M, N, K, bits, group_size, cols=None):
+    """Fused gate+up: W holds [gate | up] along N (N = 2I); returns h [M][len(cols) or I]
+    with h[:, j] = SiLU(x.W[:, j]) * (x.W[:, I + j])."""
+    I = N // 2
+    cols = np.arange(I, dtype=np.int32) if cols is None else np.asarray(cols, np.int32)
+    both = np.concatenate([cols, cols + I]).astype(np.int32)
+    y = linear(x, dtype, qweight, scales, zeros, mode, lut, g_idx, M, N, K, bits, group_size, both)
+    return swiglu(y[:, :cols.size], y[:, cols.size:])
 
 
 def linear(x, dtype, qweight, scales, zeros, mode, lut, g_idx, M, N, K, bits, group_size, cols=None):

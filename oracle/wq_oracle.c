@@ -377,3 +377,16 @@ void wqo_decode_array(const uint16_t* h, size_t n, int dtype, double* out) {
 void wqo_encode_array(const double* v, size_t n, int dtype, uint16_t* out) {
   for (size_t i = 0; i < n; ++i) out[i] = encode_act(v[i], dtype);
 }
+
+/*
+ * Activation-fused FFN input projection: h = SiLU(g) * u elementwise, with
+ * g = x . W_gate and u = x . W_up the two halves of a fused gate+up product
+ * (Triton GPTQ page, "How It Works": FFN layers fused).  The page does not
+ * name the activation; SiLU(v) = v / (1 + exp(-v)) is the reading taken.
+ * fp64 throughout.
+ */
+double wqo_silu(double v) { return v / (1.0 + exp(-v)); }
+
+void wqo_swiglu(const double* g, const double* u, size_t n, double* h) {
+  for (size_t i = 0; i < n; ++i) h[i] = wqo_silu(g[i]) * u[i];
+}

@@ -15,7 +15,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "wq_oracle.c")
 PINS = ["tests/test_oracle_formats.py", "tests/test_oracle_packing.py",
-        "tests/test_oracle_dequant.py", "tests/test_oracle_linear.py"]
+        "tests/test_oracle_dequant.py", "tests/test_oracle_linear.py", "tests/test_oracle_swiglu.py"]
 
 MUTANTS = {
     "zero_sign": ("e = s * ((double)q - z);", "e = s * ((double)q + z);"),
@@ -38,6 +38,10 @@ MUTANTS = {
                              "z = wqo_f16_to_f64(((const uint16_t*)L->zeros)[(size_t)g * L->N + (n ^ 1)]);"),
     "packed_zero_row": ("z = (double)stream_code((const uint32_t*)L->zeros + (size_t)g * wpr, 1, n, L->bits);",
                         "z = (double)stream_code((const uint32_t*)L->zeros, 1, n, L->bits);"),
+    "silu_sign": ("double wqo_silu(double v) { return v / (1.0 + exp(-v)); }",
+                  "double wqo_silu(double v) { return v / (1.0 + exp(v)); }"),
+    "swiglu_dropped_up": ("for (size_t i = 0; i < n; ++i) h[i] = wqo_silu(g[i]) * u[i];",
+                          "for (size_t i = 0; i < n; ++i) h[i] = wqo_silu(g[i]);"),
     "bf16_as_f16": ("return dtype == WQO_BF16 ? wqo_f64_to_bf16(v) : wqo_f64_to_f16(v);",
                     "return wqo_f64_to_f16(v);"),
 }
