@@ -155,6 +155,38 @@ wq_status wq_gemm(const void* x, wq_dtype dt, const void* packed, wq_qmode mode,
                   const uint16_t* lut, const int32_t* perm, void* y, int M, int N, int K,
                   int bits, int group_size, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Activation-fused gate+up layer.  The Triton GPTQ page fuses the feed-forward
+ * layers ("How It Works") without naming the activation; these entry points
+ * read it as the gated SiLU of LLaMA-style blocks: for a weight W = [gate | up]
+ * concatenated along N (N = 2I, each half quantised on its own, columns
+ * 0..I-1 the gate, I..2I-1 the up projection)
+ *     h [M][I] = SiLU(x . dequant(gate)) * (x . dequant(up)),  SiLU(v) = v / (1 + e^-v),
+ * written once, so the two products are never stored and no second kernel
+ * reads them back.
+ *
+ * wq_repack_gate_up -- the same conversion as wq_repack (same arguments, same
+ *   canonical inputs, same wq_packed_bytes size), with N % 32 == 0 required,
+ *   that interleaves the 16-column tiles of the two halves (gate tile j, then
+ *   up tile j) so one workgroup owns both halves of an output tile.  Such a
+ *   buffer is only meaningful to the *_gate_up products; wq_dequant_debug
+ *   writes its columns in that interleaved order.
+ * wq_gemv_gate_up / wq_gemm_gate_up -- h as above from a wq_repack_gate_up
+ *   buffer; same arguments and limits as wq_gemv / wq_gemm, N is the full
+ *   width 2I (N % 32 == 0, else WQ_EUNSUPPORTED) and y is h [M][N/2].  Gate
+ *   and up are each accumulated in fp32 as in wq_gemv / wq_gemm; SiLU and the
+ *   product are evaluated in fp32 and rounded to `dt` once (RNE).
+ */
+wq_status wq_repack_gate_up(const uint32_t* qweight, const uint16_t* scales, const void* zeros,
+                            wq_qmode mode, const int32_t* g_idx_host, int K, int N, int bits,
+                            int group_size, void* packed, int32_t* perm, void* stream);
+wq_status wq_gemv_gate_up(const void* x, wq_dtype dt, const void* packed, wq_qmode mode,
+                          const uint16_t* lut, const int32_t* perm, void* y, int M, int N, int K,
+                          int bits, int group_size, void* ws, size_t ws_bytes, void* stream);
+wq_status wq_gemm_gate_up(const void* x, wq_dtype dt, const void* packed, wq_qmode mode,
+                          const uint16_t* lut, const int32_t* perm, void* y, int M, int N, int K,
+                          int bits, int group_size, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -29,7 +29,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for required in ("wq_repack", "wq_dequant_debug", "wq_gemv", "wq_gemm", "wq_packed_bytes",
-                     "wq_workspace_bytes", "wq_status_str", "wq_layout_version"):
+                     "wq_workspace_bytes", "wq_status_str", "wq_layout_version",
+                     "wq_repack_gate_up", "wq_gemv_gate_up", "wq_gemm_gate_up"):
         assert required in names
 
 
@@ -72,7 +73,7 @@ def call_product(L, fn, M=1, N=4096, K=4096, bits=4, gs=128, mode=0, dt=0, x=16,
                           M, N, K, bits, gs, P(ws) if ws else None, ws_bytes, None)
 
 
-@pytest.mark.parametrize("fn", ["wq_gemv", "wq_gemm"])
+@pytest.mark.parametrize("fn", ["wq_gemv", "wq_gemm", "wq_gemv_gate_up", "wq_gemm_gate_up"])
 def test_product_rejects_before_launch(L, fn):
     # fake, never-dereferenced pointers: validation must return before any launch
     assert call_product(L, fn, bits=5) == 1                      # WQ_EINVAL
@@ -93,11 +94,20 @@ def test_product_rejects_before_launch(L, fn):
 
 def test_gemv_rejects_large_m(L):
     assert call_product(L, "wq_gemv", M=17) == 2
+    assert call_product(L, "wq_gemv_gate_up", M=17) == 2
 
 
-def test_repack_rejects_before_launch(L):
+@pytest.mark.parametrize("fn", ["wq_gemv_gate_up", "wq_gemm_gate_up"])
+def test_gate_up_needs_whole_tile_pairs(L, fn):
+    # the gate and up halves must each be a whole number of 16-column tiles
+    assert call_product(L, fn, N=4112) == 2
+    assert call_product(L, fn, N=4112, M=0) == 2
+
+
+@pytest.mark.parametrize("fn", ["wq_repack", "wq_repack_gate_up"])
+def test_repack_rejects_before_launch(L, fn):
     P = ctypes.c_void_p
-    f = L.wq_repack
+    f = getattr(L, fn)
     ok = dict(q=P(16), s=P(16), z=None, mode=0, g=None, K=4096, N=4096, bits=4, gs=128, out=P(16), perm=None)
 
     def call(**kw):
@@ -107,13 +117,16 @@ def test_repack_rejects_before_launch(L):
 
     assert call(q=None) == 1
     assert call(mode=1) == 1                # fp16 zero-points missing
-    assert call(mode=2, bits=3, N=4112, z=P(16)) == 1  # packed 3-bit zeros need N*3 % 32 == 0
+    # packed 3-bit zeros need N*3 % 32 == 0 (the gate+up repack rejects N % 32 first)
+    assert call(mode=2, bits=3, N=4112, z=P(16)) == (1 if fn == "wq_repack" else 2)
     assert call(bits=3, K=4000) == 1
     g = (ctypes.c_int32 * 4096)(*([0] * 4096))
     assert call(g=ctypes.cast(g, P)) == 1   # g_idx without a perm buffer
     assert call(g=ctypes.cast(g, P), perm=P(16)) == 2  # unbalanced groups: unsupported
     bad = (ctypes.c_int32 * 4096)(*([99] * 4096))
     assert call(g=ctypes.cast(bad, P), perm=P(16)) == 1  # group index out of range
+    if fn == "wq_repack_gate_up":
+        assert call(N=4112) == 2            # halves must be whole 16-column tiles
 
 
 def test_dequant_debug_rejects_before_launch(L):

@@ -48,11 +48,13 @@ def lib() -> ctypes.CDLL:
         L.wq_packed_bytes.restype = Z
         L.wq_workspace_bytes.argtypes = [I, I, I, I, I]
         L.wq_workspace_bytes.restype = Z
-        L.wq_repack.argtypes = [P, P, P, I, P, I, I, I, I, P, P, P]
-        L.wq_repack.restype = I
+        for name in ("wq_repack", "wq_repack_gate_up"):
+            f = getattr(L, name)
+            f.argtypes = [P, P, P, I, P, I, I, I, I, P, P, P]
+            f.restype = I
         L.wq_dequant_debug.argtypes = [P, I, P, P, I, I, I, I, I, P, P]
         L.wq_dequant_debug.restype = I
-        for name in ("wq_gemv", "wq_gemm"):
+        for name in ("wq_gemv", "wq_gemm", "wq_gemv_gate_up", "wq_gemm_gate_up"):
             f = getattr(L, name)
             f.argtypes = [P, I, P, I, P, P, P, I, I, I, I, I, P, Z, P]
             f.restype = I
@@ -108,14 +110,10 @@ class PackedLayer:
     mode: int
     lut: Optional[torch.Tensor] = None   # fp16 [2^bits] (table mode)
     perm: Optional[torch.Tensor] = None  # int32 [K] (act-order)
+    gate_up: bool = False                # repacked by wq_repack_gate_up (interleaved halves)
 
 
-def wq_repack(qweight: torch.Tensor, scales: torch.Tensor, zeros: Optional[torch.Tensor], mode: int,
-              g_idx, K: int, N: int, bits: int, group_size: int, lut: Optional[torch.Tensor] = None,
-              stream=None) -> PackedLayer:
-    """Canonical GPTQ-style tensors (device: qweight int32 [K*bits/32][N], scales fp16
-    [G][N], zeros fp16 [G][N] or int32 [G][N*bits/32]) -> PackedLayer.  g_idx: host
-    int32 array-like [K] or None."""
+def _repack(fn: str, qweight, scales, zeros, mode, g_idx, K, N, bits, group_size, lut, stream) -> PackedLayer:
     dev = qweight.device
     nbytes = wq_packed_bytes(K, N, bits, group_size, mode)
     if nbytes == 0:
@@ -127,11 +125,29 @@ def wq_repack(qweight: torch.Tensor, scales: torch.Tensor, zeros: Optional[torch
         import numpy as np
         g_host = np.ascontiguousarray(torch.as_tensor(g_idx).cpu().numpy(), dtype=np.int32)
         perm = torch.empty(K, dtype=torch.int32, device=dev)
-    rc = lib().wq_repack(_ptr(qweight), _ptr(scales), _ptr(zeros), mode,
-                         None if g_host is None else ctypes.c_void_p(g_host.ctypes.data),
-                         K, N, bits, group_size, _ptr(packed), _ptr(perm), _stream(stream))
-    _check("wq_repack", rc)
-    return PackedLayer(packed, K, N, bits, group_size, mode, lut, perm)
+    rc = getattr(lib(), fn)(_ptr(qweight), _ptr(scales), _ptr(zeros), mode,
+                            None if g_host is None else ctypes.c_void_p(g_host.ctypes.data),
+                            K, N, bits, group_size, _ptr(packed), _ptr(perm), _stream(stream))
+    _check(fn, rc)
+    return PackedLayer(packed, K, N, bits, group_size, mode, lut, perm, fn == "wq_repack_gate_up")
+
+
+def wq_repack(qweight: torch.Tensor, scales: torch.Tensor, zeros: Optional[torch.Tensor], mode: int,
+              g_idx, K: int, N: int, bits: int, group_size: int, lut: Optional[torch.Tensor] = None,
+              stream=None) -> PackedLayer:
+    """Canonical GPTQ-style tensors (device: qweight int32 [K*bits/32][N], scales fp16
+    [G][N], zeros fp16 [G][N] or int32 [G][N*bits/32]) -> PackedLayer.  g_idx: host
+    int32 array-like [K] or None."""
+    return _repack("wq_repack", qweight, scales, zeros, mode, g_idx, K, N, bits, group_size, lut, stream)
+
+
+def wq_repack_gate_up(qweight: torch.Tensor, scales: torch.Tensor, zeros: Optional[torch.Tensor], mode: int,
+                      g_idx, K: int, N: int, bits: int, group_size: int, lut: Optional[torch.Tensor] = None,
+                      stream=None) -> PackedLayer:
+    """Like wq_repack for a [gate | up] layer (N = 2I, N % 32 == 0); the result feeds
+    wq_gemv_gate_up / wq_gemm_gate_up."""
+    return _repack("wq_repack_gate_up", qweight, scales, zeros, mode, g_idx, K, N, bits, group_size, lut,
+                   stream)
 
 
 def wq_dequant_debug(layer: PackedLayer, dtype: torch.dtype, stream=None) -> torch.Tensor:
@@ -148,8 +164,12 @@ def _product(fn: str, x: torch.Tensor, layer: PackedLayer, out: Optional[torch.T
     if x.dim() != 2 or x.shape[1] != layer.K or not x.is_contiguous():
         raise ValueError("x must be a contiguous [M][K] tensor")
     M = x.shape[0]
+    fused = fn.endswith("_gate_up")
+    if fused != layer.gate_up:
+        raise ValueError(f"{fn} needs a layer repacked by "
+                         f"{'wq_repack_gate_up' if fused else 'wq_repack'}")
     if out is None:
-        out = torch.empty((M, layer.N), dtype=x.dtype, device=x.device)
+        out = torch.empty((M, layer.N // 2 if fused else layer.N), dtype=x.dtype, device=x.device)
     need = wq_workspace_bytes(M, layer.N, layer.K, layer.bits, layer.perm is not None)
     if need and (ws is None or ws.numel() * ws.element_size() < need):
         ws = torch.empty(need, dtype=torch.uint8, device=x.device)
@@ -171,6 +191,20 @@ def wq_gemm(x: torch.Tensor, layer: PackedLayer, out=None, ws=None, stream=None)
     return _product("wq_gemm", x, layer, out, ws, stream)
 
 
+def wq_gemv_gate_up(x: torch.Tensor, layer: PackedLayer, out=None, ws=None, stream=None) -> torch.Tensor:
+    """h [M][N/2] = SiLU(x . gate) * (x . up) for 1 <= M <= 16."""
+    return _product("wq_gemv_gate_up", x, layer, out, ws, stream)
+
+
+def wq_gemm_gate_up(x: torch.Tensor, layer: PackedLayer, out=None, ws=None, stream=None) -> torch.Tensor:
+    """h [M][N/2] = SiLU(x . gate) * (x . up) for any M."""
+    return _product("wq_gemm_gate_up", x, layer, out, ws, stream)
+
+
 def linear(x: torch.Tensor, layer: PackedLayer, out=None, ws=None, stream=None) -> torch.Tensor:
-    """Decode-sized M goes to wq_gemv, larger M to wq_gemm."""
-    return (wq_gemv if x.shape[0] <= 16 else wq_gemm)(x, layer, out, ws, stream)
+    """Decode-sized M goes to wq_gemv, larger M to wq_gemm (the *_gate_up pair for a
+    layer from wq_repack_gate_up)."""
+    small = x.shape[0] <= 16
+    if layer.gate_up:
+        return (wq_gemv_gate_up if small else wq_gemm_gate_up)(x, layer, out, ws, stream)
+    return (wq_gemv if small else wq_gemm)(x, layer, out, ws, stream)

@@ -50,16 +50,23 @@ __device__ inline void place_code(uint32_t* w, int kb, int e, uint32_t q) {
   }
 }
 
+// Source column tile of destination tile nt.  For a fused gate+up layer
+// ([gate | up] along N) the tiles are interleaved gate, up, gate, up, ... so
+// that the two halves of every output column sit in adjacent tiles.
+__device__ inline int source_tile(int nt, int ntiles, int gate_up) {
+  return gate_up ? ((nt & 1) ? ntiles / 2 + (nt >> 1) : (nt >> 1)) : nt;
+}
+
 // One thread per lane-slot of a tile: grid (ktiles, ntiles), block 64.
 template <int BITS, bool TABLE_LAYOUT>
 __global__ void repack_codes_kernel(const uint32_t* __restrict__ qw, const int32_t* __restrict__ perm,
-                                    int N, int ktiles, uint32_t* __restrict__ out) {
+                                    int N, int ktiles, int gate_up, uint32_t* __restrict__ out) {
   constexpr int KT = BITS == 2 ? 256 : 128;
   constexpr int KB = KT / 32;
   constexpr int WPL = BITS == 3 ? 3 : 4;
   const int lane = threadIdx.x, kt = blockIdx.x, nt = blockIdx.y;
   const int c = lane & 15, h = lane >> 4;
-  const int n = nt * 16 + c;
+  const int n = source_tile(nt, (int)gridDim.y, gate_up) * 16 + c;
   uint32_t w[4] = {0u, 0u, 0u, 0u};
   for (int kb = 0; kb < KB; ++kb) {
     for (int e = 0; e < 8; ++e) {
@@ -75,10 +82,10 @@ __global__ void repack_codes_kernel(const uint32_t* __restrict__ qw, const int32
 // Scale records: [G][N] (+ fp16 zero-points [G][N]) -> [N/16][R][16][GPU]
 // (pairs (s, z) when zeros16 is given).  grid (R, ntiles), block 16 * gpu.
 __global__ void repack_scales_kernel(const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros16,
-                                     int N, int nrec, int gpu, void* __restrict__ dst) {
+                                     int N, int nrec, int gpu, int gate_up, void* __restrict__ dst) {
   const int c = threadIdx.x / gpu, j = threadIdx.x % gpu, rec = blockIdx.x, nt = blockIdx.y;
   const int g = rec * gpu + j;
-  const size_t src = (size_t)g * N + nt * 16 + c;
+  const size_t src = (size_t)g * N + source_tile(nt, (int)gridDim.y, gate_up) * 16 + c;
   const size_t o = (((size_t)nt * nrec + rec) * 16 + c) * gpu + j;
   if (zeros16)
     ((uint32_t*)dst)[o] = (uint32_t)scales[src] | ((uint32_t)zeros16[src] << 16);
@@ -90,7 +97,7 @@ __global__ void repack_scales_kernel(const uint16_t* __restrict__ scales, const 
 // -> per (column tile, record, half, group in record) one word of 8 nibbles.
 template <int BITS>
 __global__ void repack_zeros_packed_kernel(const uint32_t* __restrict__ zp, int N, int nrec, int gpu, int ntiles,
-                                           uint32_t* __restrict__ dst) {
+                                           int gate_up, uint32_t* __restrict__ dst) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;  // ((nt * nrec + rec) * 2 + half) * gpu + j
   if (i >= ntiles * nrec * 2 * gpu) return;
   const int j = i % gpu, half = (i / gpu) % 2, rec = (i / (2 * gpu)) % nrec, nt = i / (2 * gpu * nrec);
@@ -98,7 +105,7 @@ __global__ void repack_zeros_packed_kernel(const uint32_t* __restrict__ zp, int 
   const size_t wpr = (size_t)N * BITS / 32;
   uint32_t word = 0;
   for (int c = 0; c < 8; ++c) {
-    const uint32_t bit = (uint32_t)BITS * (uint32_t)(nt * 16 + 8 * half + c);
+    const uint32_t bit = (uint32_t)BITS * (uint32_t)(source_tile(nt, ntiles, gate_up) * 16 + 8 * half + c);
     const uint32_t r = bit >> 5, sh = bit & 31;
     uint32_t v = zp[g * wpr + r] >> sh;
     if (sh + BITS > 32) v |= zp[g * wpr + r + 1] << (32 - sh);
@@ -205,11 +212,12 @@ size_t wq_workspace_bytes(int M, int N, int K, int bits, int has_perm) {
   return (size_t)M * K * 2;
 }
 
-wq_status wq_repack(const uint32_t* qweight, const uint16_t* scales, const void* zeros, wq_qmode mode,
-                    const int32_t* g_idx_host, int K, int N, int bits, int group_size, void* packed,
-                    int32_t* perm, void* stream) {
+static wq_status repack(const uint32_t* qweight, const uint16_t* scales, const void* zeros, wq_qmode mode,
+                        const int32_t* g_idx_host, int K, int N, int bits, int group_size, void* packed,
+                        int32_t* perm, void* stream, int gate_up) {
   wq_status st = check_layer(K, N, bits, group_size, mode);
   if (st != WQ_OK) return st;
+  if (gate_up && N % 32 != 0) return WQ_EUNSUPPORTED;
   if (!qweight || !scales || !packed) return WQ_EINVAL;
   if ((mode == ZERO_F16 || mode == ZERO_PACKED) && !zeros) return WQ_EINVAL;
   if (mode == ZERO_PACKED && ((long)N * bits) % 32 != 0) return WQ_EINVAL;
@@ -242,33 +250,45 @@ wq_status wq_repack(const uint32_t* qweight, const uint16_t* scales, const void*
 #define WQ_REPACK_CODES(B)                                                                              \
   if (table_layout)                                                                                     \
     hipLaunchKernelGGL((repack_codes_kernel<B, true>), grid, dim3(64), 0, s, qweight, dperm, N, L.ktiles, \
-                       (uint32_t*)(out + L.codes_off));                                                 \
+                       gate_up, (uint32_t*)(out + L.codes_off));                                        \
   else                                                                                                  \
     hipLaunchKernelGGL((repack_codes_kernel<B, false>), grid, dim3(64), 0, s, qweight, dperm, N, L.ktiles, \
-                       (uint32_t*)(out + L.codes_off));
+                       gate_up, (uint32_t*)(out + L.codes_off));
   if (bits == 4) { WQ_REPACK_CODES(4) }
   else if (bits == 3) { WQ_REPACK_CODES(3) }
   else { WQ_REPACK_CODES(2) }
 #undef WQ_REPACK_CODES
   hipLaunchKernelGGL(repack_scales_kernel, dim3(L.nrec, L.ntiles), dim3(16 * L.gpu), 0, s, scales,
-                     mode == ZERO_F16 ? (const uint16_t*)zeros : nullptr, N, L.nrec, L.gpu,
+                     mode == ZERO_F16 ? (const uint16_t*)zeros : nullptr, N, L.nrec, L.gpu, gate_up,
                      (void*)(out + L.scales_off));
   if (mode == ZERO_PACKED) {
     const int words = L.ntiles * L.nrec * 2 * L.gpu;
     dim3 g2((words + 255) / 256);
     if (bits == 4)
       hipLaunchKernelGGL(repack_zeros_packed_kernel<4>, g2, dim3(256), 0, s, (const uint32_t*)zeros, N, L.nrec,
-                         L.gpu, L.ntiles, (uint32_t*)(out + L.zeros_off));
+                         L.gpu, L.ntiles, gate_up, (uint32_t*)(out + L.zeros_off));
     else if (bits == 3)
       hipLaunchKernelGGL(repack_zeros_packed_kernel<3>, g2, dim3(256), 0, s, (const uint32_t*)zeros, N, L.nrec,
-                         L.gpu, L.ntiles, (uint32_t*)(out + L.zeros_off));
+                         L.gpu, L.ntiles, gate_up, (uint32_t*)(out + L.zeros_off));
     else
       hipLaunchKernelGGL(repack_zeros_packed_kernel<2>, g2, dim3(256), 0, s, (const uint32_t*)zeros, N, L.nrec,
-                         L.gpu, L.ntiles, (uint32_t*)(out + L.zeros_off));
+                         L.gpu, L.ntiles, gate_up, (uint32_t*)(out + L.zeros_off));
   }
   if ((st = launch_status()) != WQ_OK) return st;
   // host_perm is read by the copy above: wait before it goes out of scope.
   return hipStreamSynchronize(s) == hipSuccess ? WQ_OK : WQ_EHIP;
+}
+
+wq_status wq_repack(const uint32_t* qweight, const uint16_t* scales, const void* zeros, wq_qmode mode,
+                    const int32_t* g_idx_host, int K, int N, int bits, int group_size, void* packed,
+                    int32_t* perm, void* stream) {
+  return repack(qweight, scales, zeros, mode, g_idx_host, K, N, bits, group_size, packed, perm, stream, 0);
+}
+
+wq_status wq_repack_gate_up(const uint32_t* qweight, const uint16_t* scales, const void* zeros, wq_qmode mode,
+                            const int32_t* g_idx_host, int K, int N, int bits, int group_size, void* packed,
+                            int32_t* perm, void* stream) {
+  return repack(qweight, scales, zeros, mode, g_idx_host, K, N, bits, group_size, packed, perm, stream, 1);
 }
 
 wq_status wq_dequant_debug(const void* packed, wq_qmode mode, const uint16_t* lut, const int32_t* perm, int K,
@@ -301,7 +321,7 @@ wq_status wq_dequant_debug(const void* packed, wq_qmode mode, const uint16_t* lu
   return launch_status();
 }
 
-static wq_status product(bool gemm, const void* x, wq_dtype dt, const void* packed, wq_qmode mode,
+static wq_status product(bool gemm, bool swiglu, const void* x, wq_dtype dt, const void* packed, wq_qmode mode,
                          const uint16_t* lut, const int32_t* perm, void* y, int M, int N, int K, int bits,
                          int group_size, void* ws, size_t ws_bytes, void* stream) {
   wq_status st = check_layer(K, N, bits, group_size, mode);
@@ -309,6 +329,7 @@ static wq_status product(bool gemm, const void* x, wq_dtype dt, const void* pack
   if (M < 0) return WQ_EINVAL;
   if (dt != WQ_F16 && dt != WQ_BF16) return WQ_EINVAL;
   if (!gemm && M > 16) return WQ_EUNSUPPORTED;
+  if (swiglu && N % 32 != 0) return WQ_EUNSUPPORTED;
   if (M == 0) return WQ_OK;
   if (!x || !packed || !y) return WQ_EINVAL;
   if (mode == LUT && !lut) return WQ_EINVAL;
@@ -327,20 +348,32 @@ static wq_status product(bool gemm, const void* x, wq_dtype dt, const void* pack
     if ((st = launch_status()) != WQ_OK) return st;
     xin = ws;
   }
-  ProductArgs a{xin, (int)dt, packed, (int)mode, lut, y, M, N, K, bits, group_size, s};
+  ProductArgs a{xin, (int)dt, packed, (int)mode, lut, y, M, N, K, bits, group_size, swiglu ? 1 : 0, s};
   return launch_product(gemm, a);
 }
 
 wq_status wq_gemv(const void* x, wq_dtype dt, const void* packed, wq_qmode mode, const uint16_t* lut,
                   const int32_t* perm, void* y, int M, int N, int K, int bits, int group_size, void* ws,
                   size_t ws_bytes, void* stream) {
-  return product(false, x, dt, packed, mode, lut, perm, y, M, N, K, bits, group_size, ws, ws_bytes, stream);
+  return product(false, false, x, dt, packed, mode, lut, perm, y, M, N, K, bits, group_size, ws, ws_bytes, stream);
 }
 
 wq_status wq_gemm(const void* x, wq_dtype dt, const void* packed, wq_qmode mode, const uint16_t* lut,
                   const int32_t* perm, void* y, int M, int N, int K, int bits, int group_size, void* ws,
                   size_t ws_bytes, void* stream) {
-  return product(true, x, dt, packed, mode, lut, perm, y, M, N, K, bits, group_size, ws, ws_bytes, stream);
+  return product(true, false, x, dt, packed, mode, lut, perm, y, M, N, K, bits, group_size, ws, ws_bytes, stream);
+}
+
+wq_status wq_gemv_gate_up(const void* x, wq_dtype dt, const void* packed, wq_qmode mode, const uint16_t* lut,
+                          const int32_t* perm, void* y, int M, int N, int K, int bits, int group_size, void* ws,
+                          size_t ws_bytes, void* stream) {
+  return product(false, true, x, dt, packed, mode, lut, perm, y, M, N, K, bits, group_size, ws, ws_bytes, stream);
+}
+
+wq_status wq_gemm_gate_up(const void* x, wq_dtype dt, const void* packed, wq_qmode mode, const uint16_t* lut,
+                          const int32_t* perm, void* y, int M, int N, int K, int bits, int group_size, void* ws,
+                          size_t ws_bytes, void* stream) {
+  return product(true, true, x, dt, packed, mode, lut, perm, y, M, N, K, bits, group_size, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -51,6 +51,7 @@ struct ProductArgs {
   const uint16_t* lut;
   void* y;
   int M, N, K, bits, group_size;
+  int swiglu;               // 1: fused gate+up layer, y [M][N/2] = SiLU(gate) * up
   hipStream_t stream;
 };
 #define WQ_CAT2(a, b) a##b

@@ -40,6 +40,7 @@ struct GemmArgs {
   uint16_t* y;
   uint32_t codes_bytes, s_bytes, z_bytes;
   int M, N, K, nrec, upr, ktiles, ntiles, mtiles, ntiles_wg;  // upr: 128-row units per metadata record
+  int swiglu;             // fused gate+up layer: y [M][N/2] = SiLU(gate) * up
 };
 
 // s_waitcnt immediate (gfx9 encoding) that waits until at most n vector
@@ -254,24 +255,56 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
   //      activations as B, so they produce y transposed: lane (c, h) holds
   //      row m0 + 16 i + c, columns 4h .. 4h + 3 of column tile t -- four
   //      consecutive outputs, one 8-byte store.
+  auto col_scales = [&](int t, float (&s)[4]) {
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    if (nt0 + t >= a.ntiles) continue;
-    const int n = (nt0 + t) * 16 + 4 * h;
-    float s[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+    for (int e = 0; e < 4; ++e) s[e] = 1.0f;
     if constexpr (EPI_SCALE) {  // one scale record per column tile
       typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
       const u16x4 sv = *(const u16x4*)(a.S + (size_t)(nt0 + t) * 16 + 4 * h);
 #pragma unroll
       for (int e = 0; e < 4; ++e) s[e] = f16_to_f32(sv[e]);
     }
+  };
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  if (a.swiglu) {
+    // Fused gate+up layer: column tiles are interleaved (gate, up, ...), so
+    // tiles 2p and 2p + 1 of the wave are the gate and up halves of output
+    // tile nt0 / 2 + p (nt0 is a multiple of 4 and the tile count even).
+#pragma unroll
+    for (int p = 0; p < NT / 2; ++p) {
+      if (nt0 + 2 * p >= a.ntiles) continue;
+      float sg[4], su[4];
+      col_scales(2 * p, sg);
+      col_scales(2 * p + 1, su);
+      const int n = (nt0 / 2 + p) * 16 + 4 * h;
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        const int m = m0 + 16 * i + c;
+        if (m < a.M) {
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float g = acc[i][2 * p][e] * sg[e];
+            v[e] = g / (1.0f + expf(-g)) * (acc[i][2 * p + 1][e] * su[e]);
+          }
+          *(u32x2*)(a.y + (size_t)m * (a.N / 2) + n) = u32x2{pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
+        }
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    if (nt0 + t >= a.ntiles) continue;
+    const int n = (nt0 + t) * 16 + 4 * h;
+    float s[4];
+    col_scales(t, s);
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
       const int m = m0 + 16 * i + c;
       if (m < a.M) {
         const uint32_t lo = pack2<DT>(acc[i][t][0] * s[0], acc[i][t][1] * s[1]);
         const uint32_t hi = pack2<DT>(acc[i][t][2] * s[2], acc[i][t][3] * s[3]);
-        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
         *(u32x2*)(a.y + (size_t)m * a.N + n) = u32x2{lo, hi};
       }
     }
@@ -311,6 +344,7 @@ wq_status WQ_CAT(launch_gemm_, WQ_VARIANT)(const ProductArgs& p) {
   g.M = p.M; g.N = p.N; g.K = p.K; g.nrec = L.nrec; g.upr = (L.gsz > 128 ? L.gsz : 128) / 128;
   g.ktiles = L.ktiles; g.ntiles = L.ntiles;
   g.mtiles = 0; g.ntiles_wg = 0;
+  g.swiglu = p.swiglu;
   const int gpu = L.gsz >= 128 ? 1 : 128 / L.gsz;
   const bool epi = L.G == 1 && p.mode == SYM && D == F16;
   wq_status st = WQ_EINVAL;

@@ -41,6 +41,7 @@ struct GemvArgs {
   uint16_t* y;            // [M][N]
   uint32_t codes_bytes, s_bytes, z_bytes;
   int M, N, K, nrec, upr, ktiles, waves, kt_per_wave;  // upr: 128-row units per metadata record
+  int ldy;                // row stride of y (N, or N / 2 for a fused gate+up layer)
 };
 
 // Decode k-block KB of a tile into a B operand.
@@ -59,7 +60,10 @@ __device__ inline float zero_corr(float z) {
 }
 
 // Waves per workgroup are chosen at launch (1..16); the bound below lets 16.
-template <int DT, int BITS, int MODE, int TN, int GPU, bool PACKED, int PF>
+// SWIGLU: the layer is a fused gate+up layer repacked with interleaved column
+// tiles (gate, up, gate, up, ...); tiles 2p and 2p+1 of a workgroup are the
+// two halves of one output tile and the store writes SiLU(gate) * up.
+template <int DT, int BITS, int MODE, int TN, int GPU, bool PACKED, int PF, bool SWIGLU>
 __global__ __launch_bounds__(1024) void gemv_kernel(const GemvArgs a) {
   constexpr int KT = BITS == 2 ? 256 : 128;
   constexpr int UPT = KT / 128;                 // 128-row units per tile
@@ -261,26 +265,38 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const GemvArgs a) {
     }
   }
   __syncthreads();
-  constexpr int SLOTS = TN * NRED * 64;
+  constexpr int OUTS = SWIGLU ? TN / 2 : TN;  // output column tiles of the workgroup
+  constexpr int SLOTS = OUTS * NRED * 64;
   for (int i = threadIdx.x; i < SLOTS; i += a.waves * 64) {
-    const int l = i & 63, e = (i >> 6) % NRED, t = i / (64 * NRED);
-    float v = 0.0f;
-    for (int w = 0; w < a.waves; ++w) v += red[((size_t)(w * TN + t) * NRED + e) * 64 + l];
+    const int l = i & 63, e = (i >> 6) % NRED, o = i / (64 * NRED);
+    auto reduce = [&](int t) {
+      float v = 0.0f;
+      for (int w = 0; w < a.waves; ++w) v += red[((size_t)(w * TN + t) * NRED + e) * 64 + l];
+      return v;
+    };
+    float v;
+    if constexpr (SWIGLU) {
+      const float g = reduce(2 * o), u = reduce(2 * o + 1);
+      v = g / (1.0f + expf(-g)) * u;
+    } else {
+      v = reduce(o);
+    }
     // packed: lane l = 16 m + col ; standard: row 4 (l / 16) + e, col l % 16
     const int m = PACKED ? (l >> 4) : 4 * (l >> 4) + e;
-    const int n = (nt0 + t) * 16 + (l & 15);
-    if (m < a.M) a.y[(size_t)m * a.N + n] = DT == F16 ? f32_to_f16(v) : f32_to_bf16(v);
+    const int n = (SWIGLU ? nt0 / 2 + o : nt0 + o) * 16 + (l & 15);
+    if (m < a.M) a.y[(size_t)m * a.ldy + n] = DT == F16 ? f32_to_f16(v) : f32_to_bf16(v);
   }
 }
 
 // ---------------------------------------------------------------------------
 // Launch-shape choice and dispatch.
 // ---------------------------------------------------------------------------
-template <int DT, int BITS, int MODE, int TN, int GPU, bool PACKED, int PF>
+template <int DT, int BITS, int MODE, int TN, int GPU, bool PACKED, int PF, bool SWIGLU>
 wq_status run(GemvArgs g, int grid, hipStream_t s) {
   constexpr int NRED = PACKED ? 1 : 4;
   const size_t lds = (size_t)g.waves * TN * NRED * 64 * sizeof(float);
-  hipLaunchKernelGGL((gemv_kernel<DT, BITS, MODE, TN, GPU, PACKED, PF>), dim3(grid), dim3(g.waves * 64), lds, s, g);
+  hipLaunchKernelGGL((gemv_kernel<DT, BITS, MODE, TN, GPU, PACKED, PF, SWIGLU>), dim3(grid), dim3(g.waves * 64), lds,
+                     s, g);
   return launch_status();
 }
 
@@ -294,22 +310,31 @@ inline int pick_waves(int grid, int ktiles, int tn) {
   return w;
 }
 
-template <int DT, int BITS, int MODE, int TN, int GPU, bool PACKED>
+template <int DT, int BITS, int MODE, int TN, int GPU, bool PACKED, bool SWIGLU>
 wq_status run_pf(GemvArgs g, int grid, hipStream_t s) {
   const int tpw = g.kt_per_wave;
-  if (PACKED && tpw >= 8) return run<DT, BITS, MODE, TN, GPU, PACKED, 4>(g, grid, s);
-  if (PACKED && tpw >= 5) return run<DT, BITS, MODE, TN, GPU, PACKED, 3>(g, grid, s);
-  return run<DT, BITS, MODE, TN, GPU, PACKED, 2>(g, grid, s);
+  if (PACKED && tpw >= 8) return run<DT, BITS, MODE, TN, GPU, PACKED, 4, SWIGLU>(g, grid, s);
+  if (PACKED && tpw >= 5) return run<DT, BITS, MODE, TN, GPU, PACKED, 3, SWIGLU>(g, grid, s);
+  return run<DT, BITS, MODE, TN, GPU, PACKED, 2, SWIGLU>(g, grid, s);
 }
 
-template <int DT, int BITS, int MODE, int GPU>
+template <int DT, int BITS, int MODE, int GPU, bool SWIGLU>
 wq_status pick_shape(GemvArgs g, hipStream_t s) {
   const int ntiles = g.N / 16;
+  if (SWIGLU) {
+    // gate and up tiles of one output tile stay in one workgroup
+    const bool packed = g.M <= 4;
+    const int grid = ntiles / 2;
+    g.waves = pick_waves(grid, g.ktiles, 2);
+    g.kt_per_wave = (g.ktiles + g.waves - 1) / g.waves;
+    if (packed) return run_pf<DT, BITS, MODE, 2, GPU, true, true>(g, grid, s);
+    return run_pf<DT, BITS, MODE, 2, GPU, false, true>(g, grid, s);
+  }
   if (g.M <= 4) {
     const int grid = ntiles;
     g.waves = pick_waves(grid, g.ktiles, 1);
     g.kt_per_wave = (g.ktiles + g.waves - 1) / g.waves;
-    return run_pf<DT, BITS, MODE, 1, GPU, true>(g, grid, s);
+    return run_pf<DT, BITS, MODE, 1, GPU, true, false>(g, grid, s);
   }
   // One activation row per MFMA row; two column tiles per workgroup share the
   // activation loads when the grid stays large enough.
@@ -317,8 +342,8 @@ wq_status pick_shape(GemvArgs g, hipStream_t s) {
   const int grid = ntiles / tn;
   g.waves = pick_waves(grid, g.ktiles, tn);
   g.kt_per_wave = (g.ktiles + g.waves - 1) / g.waves;
-  if (tn == 2) return run_pf<DT, BITS, MODE, 2, GPU, false>(g, grid, s);
-  return run_pf<DT, BITS, MODE, 1, GPU, false>(g, grid, s);
+  if (tn == 2) return run_pf<DT, BITS, MODE, 2, GPU, false, false>(g, grid, s);
+  return run_pf<DT, BITS, MODE, 1, GPU, false, false>(g, grid, s);
 }
 
 }  // namespace
@@ -340,14 +365,21 @@ wq_status WQ_CAT(launch_gemv_, WQ_VARIANT)(const ProductArgs& p) {
   g.M = p.M; g.N = p.N; g.K = p.K; g.nrec = L.nrec; g.upr = (L.gsz > 128 ? L.gsz : 128) / 128;
   g.ktiles = L.ktiles;
   g.waves = 1; g.kt_per_wave = 0;
+  g.ldy = p.swiglu ? p.N / 2 : p.N;
   const int gpu = L.gsz >= 128 ? 1 : 128 / L.gsz;  // groups per 128-row unit
   wq_status st = WQ_EINVAL;
   sfor<4>([&](auto mi) {
     constexpr int MODE = decltype(mi)::value;
     if (MODE != p.mode) return;
-    if (gpu == 1) st = pick_shape<D, B, MODE, 1>(g, p.stream);
-    else if (gpu == 2) st = pick_shape<D, B, MODE, 2>(g, p.stream);
-    else st = pick_shape<D, B, MODE, 4>(g, p.stream);
+    if (p.swiglu) {
+      if (gpu == 1) st = pick_shape<D, B, MODE, 1, true>(g, p.stream);
+      else if (gpu == 2) st = pick_shape<D, B, MODE, 2, true>(g, p.stream);
+      else st = pick_shape<D, B, MODE, 4, true>(g, p.stream);
+    } else {
+      if (gpu == 1) st = pick_shape<D, B, MODE, 1, false>(g, p.stream);
+      else if (gpu == 2) st = pick_shape<D, B, MODE, 2, false>(g, p.stream);
+      else st = pick_shape<D, B, MODE, 4, false>(g, p.stream);
+    }
   });
   return st;
 }
