@@ -20,6 +20,9 @@ Also reported:
                 rotated copies between HIP events on its stream;
   gemm          the prefill layer set at M = 2048 (symmetric int4, group -1 and
                 128) through wq_gemm, as TFLOP/s against dense fp16 MFMA peak;
+  fused_gate_up the gate+up layer at M = 1 and 2048: plain product, plain
+                product + torch SiLU/multiply, and the fused SiLU(gate)*up
+                entry points;
   cpu_baseline  the CPU oracle on a bounded sample of the same step.
 """
 import argparse
@@ -46,6 +49,7 @@ def parse():
     p.add_argument("--gemm-steps", type=int, default=20)
     p.add_argument("--no-gemm", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--no-fused", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--copy-probe", action="store_true",
                    help="also run a plain device copy of known size (counter calibration)")
@@ -106,7 +110,8 @@ def main():
             return torch.from_numpy(a.view(np.int16)).view(dtype).to(dev)
         return torch.from_numpy(a.view(np.int32)).to(dev)
 
-    def repack_copies(L, copies):
+    def repack_copies(L, copies, repack=None):
+        repack = repack or wq.wq_repack
         q = to_dev(L.qweight, torch.int32)
         s = to_dev(L.scales, torch.float16)
         z = None
@@ -115,7 +120,7 @@ def main():
         elif L.mode == wl.ZERO_PACKED:
             z = to_dev(L.zeros, torch.int32)
         lut = to_dev(L.lut, torch.float16) if L.lut is not None else None
-        out = [wq.wq_repack(q, s, z, L.mode, L.g_idx, L.K, L.N, L.bits, L.group_size, lut=lut)
+        out = [repack(q, s, z, L.mode, L.g_idx, L.K, L.N, L.bits, L.group_size, lut=lut)
                for _ in range(copies)]
         del q, s, z
         return out
@@ -261,6 +266,57 @@ def main():
             del gp, gx, gy
             torch.cuda.empty_cache()
 
+    # ---------------- activation-fused gate+up ----------------
+    # The gate+up layer three ways, each over rotated copies, launches back to
+    # back between events: the plain product (y = [gate | up], no activation),
+    # the plain product followed by torch's SiLU and multiply (two more
+    # launches, y written and read back), and the fused product writing
+    # h = SiLU(gate) * up.
+    fused = None
+    if not args.no_fused:
+        Lg = cfg.layer("gate_up")
+        I = Lg.N // 2
+        Rg = max(2, -(-(1 << 30) // Lg.weight_bytes()))
+        fused = {"layer": f"gate_up {Lg.K}x{Lg.N}", "rotated_copies": Rg}
+        plain = repack_copies(Lg, Rg)
+        fpack = repack_copies(Lg, Rg, wq.wq_repack_gate_up)
+        for Mf, fn, ffn in ((1, wq.wq_gemv, wq.wq_gemv_gate_up), (2048, wq.wq_gemm, wq.wq_gemm_gate_up)):
+            xf = to_dev(cfg.x(Mf, Lg.K), torch.float16)
+            yf = torch.empty((Mf, Lg.N), dtype=torch.float16, device=dev)
+            hf = torch.empty((Mf, I), dtype=torch.float16, device=dev)
+            n = max(4 * Rg, 40) if Mf == 1 else 2 * Rg
+
+            def plain_call(i):
+                fn(xf, plain[i % Rg], out=yf, stream=stream)
+
+            def unfused_call(i):
+                fn(xf, plain[i % Rg], out=yf, stream=stream)
+                torch.mul(torch.nn.functional.silu(yf[:, :I]), yf[:, I:], out=hf)
+
+            def fused_call(i):
+                ffn(xf, fpack[i % Rg], out=hf, stream=stream)
+
+            res = {}
+            for name, call in (("plain_us", plain_call), ("unfused_torch_silu_us", unfused_call),
+                               ("fused_us", fused_call)):
+                for i in range(Rg):
+                    call(i)
+                torch.cuda.synchronize()
+                e0.record(stream)
+                for i in range(n):
+                    call(i)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                res[name] = round(e0.elapsed_time(e1) / n * 1e3, 3)
+            if Mf == 1:
+                res["fused_weight_GBps"] = round(Lg.weight_bytes() / (res["fused_us"] * 1e-6) / 1e9, 1)
+            else:
+                res["fused_tflops"] = round(2.0 * Mf * Lg.N * Lg.K / (res["fused_us"] * 1e-6) / 1e12, 1)
+            fused[f"M{Mf}"] = res
+            del xf, yf, hf
+        del plain, fpack
+        torch.cuda.empty_cache()
+
     # ---------------- plain copy (counter calibration) ----------------
     if args.copy_probe:
         src = torch.empty(1 << 28, dtype=torch.uint8, device=dev).fill_(1)
@@ -299,7 +355,8 @@ def main():
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "eager": {"ms_per_step": round(eager_ms_per_step, 5),
                   "value": round(set_bytes / (eager_ms_per_step * 1e-3) / 1e9, 1)},
-        "roofline": roofline, "per_kernel": per_kernel, "gemm_m2048": gemm, "cpu_baseline": cpu,
+        "roofline": roofline, "per_kernel": per_kernel, "gemm_m2048": gemm,
+        "fused_gate_up": fused, "cpu_baseline": cpu,
         "kernel_sources_sha256_16": khash,
     }
     print(json.dumps(out), flush=True)

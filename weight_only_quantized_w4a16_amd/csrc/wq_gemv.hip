@@ -61,8 +61,9 @@ __device__ inline float zero_corr(float z) {
 
 // Waves per workgroup are chosen at launch (1..16); the bound below lets 16.
 // SWIGLU: the layer is a fused gate+up layer repacked with interleaved column
-// tiles (gate, up, gate, up, ...); tiles 2p and 2p+1 of a workgroup are the
-// two halves of one output tile and the store writes SiLU(gate) * up.
+// tiles (gate, up, gate, up, ...).  Workgroup p owns output tile p: its even
+// waves stream gate tile 2p, its odd waves up tile 2p + 1 (TN = 1, each pair
+// of waves shares one k-range), and the store writes SiLU(gate) * up.
 template <int DT, int BITS, int MODE, int TN, int GPU, bool PACKED, int PF, bool SWIGLU>
 __global__ __launch_bounds__(1024) void gemv_kernel(const GemvArgs a) {
   constexpr int KT = BITS == 2 ? 256 : 128;
@@ -85,7 +86,8 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const GemvArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar arithmetic
   const int c = lane & 15, h = lane >> 4;
-  const int nt0 = blockIdx.x * TN;
+  const int nt0 = SWIGLU ? 2 * blockIdx.x + (wave & 1) : blockIdx.x * TN;  // first column tile of this wave
+  const int kslot = SWIGLU ? wave >> 1 : wave;                             // k-range of this wave
 
   const rsrc_t rc = make_rsrc(a.codes, a.codes_bytes);
   const rsrc_t rx = make_rsrc(a.x, (uint32_t)a.M * a.K * 2);
@@ -102,7 +104,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const GemvArgs a) {
   const uint32_t s_lane = (uint32_t)c * REC;
   const uint32_t zp_lane = (uint32_t)(c >> 3) * ZREC;
 
-  const int kt0 = wave * a.kt_per_wave;
+  const int kt0 = kslot * a.kt_per_wave;
   const int kt1 = min(kt0 + a.kt_per_wave, a.ktiles);
 
   struct Frame {
@@ -265,25 +267,26 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const GemvArgs a) {
     }
   }
   __syncthreads();
-  constexpr int OUTS = SWIGLU ? TN / 2 : TN;  // output column tiles of the workgroup
-  constexpr int SLOTS = OUTS * NRED * 64;
+  static_assert(!SWIGLU || TN == 1, "gate and up tiles sit on different waves");
+  constexpr int SLOTS = TN * NRED * 64;
   for (int i = threadIdx.x; i < SLOTS; i += a.waves * 64) {
-    const int l = i & 63, e = (i >> 6) % NRED, o = i / (64 * NRED);
-    auto reduce = [&](int t) {
+    const int l = i & 63, e = (i >> 6) % NRED, t = i / (64 * NRED);
+    // sum over the waves w0, w0 + step, ... of tile t's partial results
+    auto reduce = [&](int w0, int step) {
       float v = 0.0f;
-      for (int w = 0; w < a.waves; ++w) v += red[((size_t)(w * TN + t) * NRED + e) * 64 + l];
+      for (int w = w0; w < a.waves; w += step) v += red[((size_t)(w * TN + t) * NRED + e) * 64 + l];
       return v;
     };
     float v;
     if constexpr (SWIGLU) {
-      const float g = reduce(2 * o), u = reduce(2 * o + 1);
+      const float g = reduce(0, 2), u = reduce(1, 2);
       v = g / (1.0f + expf(-g)) * u;
     } else {
-      v = reduce(o);
+      v = reduce(0, 1);
     }
     // packed: lane l = 16 m + col ; standard: row 4 (l / 16) + e, col l % 16
     const int m = PACKED ? (l >> 4) : 4 * (l >> 4) + e;
-    const int n = (SWIGLU ? nt0 / 2 + o : nt0 + o) * 16 + (l & 15);
+    const int n = (SWIGLU ? (int)blockIdx.x : nt0 + t) * 16 + (l & 15);
     if (m < a.M) a.y[(size_t)m * a.ldy + n] = DT == F16 ? f32_to_f16(v) : f32_to_bf16(v);
   }
 }
@@ -322,13 +325,17 @@ template <int DT, int BITS, int MODE, int GPU, bool SWIGLU>
 wq_status pick_shape(GemvArgs g, hipStream_t s) {
   const int ntiles = g.N / 16;
   if (SWIGLU) {
-    // gate and up tiles of one output tile stay in one workgroup
-    const bool packed = g.M <= 4;
+    // One workgroup per output tile, its waves split between the gate and up
+    // tiles.  Half the waves per column tile of the plain product (each
+    // streaming twice the k-range) keeps the workgroup at the plain product's
+    // size; measured faster than matching its per-wave work with workgroups
+    // twice as large.
     const int grid = ntiles / 2;
-    g.waves = pick_waves(grid, g.ktiles, 2);
-    g.kt_per_wave = (g.ktiles + g.waves - 1) / g.waves;
-    if (packed) return run_pf<DT, BITS, MODE, 2, GPU, true, true>(g, grid, s);
-    return run_pf<DT, BITS, MODE, 2, GPU, false, true>(g, grid, s);
+    const int kw = max(1, min(pick_waves(ntiles, g.ktiles, 1), 8) / 2);  // waves per column tile
+    g.waves = 2 * kw;
+    g.kt_per_wave = (g.ktiles + kw - 1) / kw;
+    if (g.M <= 4) return run_pf<DT, BITS, MODE, 1, GPU, true, true>(g, grid, s);
+    return run_pf<DT, BITS, MODE, 1, GPU, false, true>(g, grid, s);
   }
   if (g.M <= 4) {
     const int grid = ntiles;
