@@ -58,6 +58,7 @@ def lib():
         L.wqo_silu.restype = ctypes.c_double
         L.wqo_swiglu.argtypes = [P, P, ctypes.c_size_t, P]
         L.wqo_swiglu.restype = None
+        L.wqo_hadamard.argtypes = [P, i, i, i, P]
         _lib = L
     return _lib
 
@@ -158,6 +159,22 @@ def swiglu(g, u):
     h = np.empty(g.shape, np.float64)
     lib().wqo_swiglu(_p(g), _p(u), g.size, _p(h))
     return h
+
+
+def hadamard(x, block):
+    """Rows of x (fp64 [M][K]) rotated by the orthonormal block-diagonal
+    Walsh-Hadamard matrix of block size `block` (fp64)."""
+    x = _c(x, np.float64)
+    M, K = x.shape
+    y = np.empty((M, K), np.float64)
+    _check(lib().wqo_hadamard(_p(x), M, K, block, _p(y)))
+    return y
+
+
+def rotate_x(x_bits, dtype, block):
+    """Activation bit patterns -> rotated activations rounded once (RNE) to the
+    activation dtype, as bit patterns."""
+    return encode(hadamard(decode(x_bits, dtype), block), dtype)
 
 
 def linear_gate_up(x, dtype, qweight, scales, zeros, mode, lut, g_idx, M, N, K, bits, group_size, cols=None):

@@ -390,3 +390,45 @@ double wqo_silu(double v) { return v / (1.0 + exp(-v)); }
 void wqo_swiglu(const double* g, const double* u, size_t n, double* h) {
   for (size_t i = 0; i < n; ++i) h[i] = wqo_silu(g[i]) * u[i];
 }
+
+/*
+ * Online Hadamard rotation of the activations (FLUTE page, "Maintenance &
+ * Community": Hadamard transform support).  The page gives no details; the
+ * reading taken is the usual one for rotated weight-only quantisation: the
+ * weights were rotated and quantised offline as H W, and at run time each
+ * activation row is rotated by the same orthonormal, block-diagonal
+ * Walsh-Hadamard matrix, so that (x H)(H W) = x W (H is symmetric and H H = I).
+ *
+ * With block size b (a power of two dividing K), for every row m and every
+ * block start k0 = 0, b, 2b, ...:
+ *     y[m][k0 + i] = b^(-1/2) * sum_j (-1)^popcount(i & j) * x[m][k0 + j]
+ * (the Sylvester construction of the b x b Hadamard matrix, entry (i, j) =
+ * (-1)^(number of bit positions where both i and j have a one)).
+ * Direct O(b^2) sum per block, fp64.  Returns 0, or 1 for bad sizes.
+ */
+static int parity_of_and(unsigned i, unsigned j) {
+  unsigned v = i & j;
+  int p = 0;
+  while (v) {
+    p ^= (int)(v & 1u);
+    v >>= 1;
+  }
+  return p;
+}
+
+int wqo_hadamard(const double* x, int M, int K, int b, double* y) {
+  if (M < 0 || K <= 0 || b <= 0 || (b & (b - 1)) != 0 || K % b != 0) return 1;
+  const double norm = 1.0 / sqrt((double)b);
+  for (int m = 0; m < M; ++m) {
+    for (int k0 = 0; k0 < K; k0 += b) {
+      const double* xb = x + (size_t)m * K + k0;
+      double* yb = y + (size_t)m * K + k0;
+      for (int i = 0; i < b; ++i) {
+        double s = 0.0;
+        for (int j = 0; j < b; ++j) s += parity_of_and((unsigned)i, (unsigned)j) ? -xb[j] : xb[j];
+        yb[i] = s * norm;
+      }
+    }
+  }
+  return 0;
+}

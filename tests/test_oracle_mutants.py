@@ -15,7 +15,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "wq_oracle.c")
 PINS = ["tests/test_oracle_formats.py", "tests/test_oracle_packing.py",
-        "tests/test_oracle_dequant.py", "tests/test_oracle_linear.py", "tests/test_oracle_swiglu.py"]
+        "tests/test_oracle_dequant.py", "tests/test_oracle_linear.py", "tests/test_oracle_swiglu.py",
+        "tests/test_oracle_hadamard.py"]
 
 MUTANTS = {
     "zero_sign": ("e = s * ((double)q - z);", "e = s * ((double)q + z);"),
@@ -42,6 +43,9 @@ MUTANTS = {
                   "double wqo_silu(double v) { return v / (1.0 + exp(v)); }"),
     "swiglu_dropped_up": ("for (size_t i = 0; i < n; ++i) h[i] = wqo_silu(g[i]) * u[i];",
                           "for (size_t i = 0; i < n; ++i) h[i] = wqo_silu(g[i]);"),
+    "hadamard_or_for_and": ("  unsigned v = i & j;", "  unsigned v = i | j;"),
+    "hadamard_norm": ("const double norm = 1.0 / sqrt((double)b);", "const double norm = 1.0 / (double)b;"),
+    "hadamard_block_offset": ("const double* xb = x + (size_t)m * K + k0;", "const double* xb = x + (size_t)m * K;"),
     "bf16_as_f16": ("return dtype == WQO_BF16 ? wqo_f64_to_bf16(v) : wqo_f64_to_f16(v);",
                     "return wqo_f64_to_f16(v);"),
 }
