@@ -23,6 +23,8 @@ Also reported:
   fused_gate_up the gate+up layer at M = 1 and 2048: plain product, plain
                 product + torch SiLU/multiply, and the fused SiLU(gate)*up
                 entry points;
+  hadamard      the online rotation of the activations alone and followed by
+                the product, on the QKV layer at M = 1 and 2048;
   cpu_baseline  the CPU oracle on a bounded sample of the same step.
 """
 import argparse
@@ -50,6 +52,7 @@ def parse():
     p.add_argument("--no-gemm", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--no-fused", action="store_true")
+    p.add_argument("--no-hadamard", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--copy-probe", action="store_true",
                    help="also run a plain device copy of known size (counter calibration)")
@@ -317,6 +320,49 @@ def main():
         del plain, fpack
         torch.cuda.empty_cache()
 
+    # ---------------- online Hadamard rotation ----------------
+    # The rotation alone (2 * M * K bytes moved) and the rotated product
+    # (rotation, then the plain product on the rotated rows) against the plain
+    # product, on the QKV layer (K = 4096, block 128), launches back to back.
+    had = None
+    if not args.no_hadamard:
+        Lq = cfg.layer("qkv")
+        Rq = max(2, -(-(1 << 30) // Lq.weight_bytes()))
+        qp = repack_copies(Lq, Rq)
+        had = {"layer": f"qkv {Lq.K}x{Lq.N}", "block": 128, "rotated_copies": Rq}
+        for Mh, fn in ((1, wq.wq_gemv), (2048, wq.wq_gemm)):
+            xh = to_dev(cfg.x(Mh, Lq.K), torch.float16)
+            xr = torch.empty_like(xh)
+            yh = torch.empty((Mh, Lq.N), dtype=torch.float16, device=dev)
+            n = max(4 * Rq, 40) if Mh == 1 else 2 * Rq
+
+            def rot(i):
+                wq.wq_hadamard(xh, 128, out=xr, stream=stream)
+
+            def prod(i):
+                fn(xh, qp[i % Rq], out=yh, stream=stream)
+
+            def rot_prod(i):
+                wq.wq_hadamard(xh, 128, out=xr, stream=stream)
+                fn(xr, qp[i % Rq], out=yh, stream=stream)
+
+            res = {}
+            for name, call in (("rotate_us", rot), ("product_us", prod), ("rotate_then_product_us", rot_prod)):
+                for i in range(Rq):
+                    call(i)
+                torch.cuda.synchronize()
+                e0.record(stream)
+                for i in range(n):
+                    call(i)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                res[name] = round(e0.elapsed_time(e1) / n * 1e3, 3)
+            res["rotate_GBps"] = round(4.0 * Mh * Lq.K / (res["rotate_us"] * 1e-6) / 1e9, 1)
+            had[f"M{Mh}"] = res
+            del xh, xr, yh
+        del qp
+        torch.cuda.empty_cache()
+
     # ---------------- plain copy (counter calibration) ----------------
     if args.copy_probe:
         src = torch.empty(1 << 28, dtype=torch.uint8, device=dev).fill_(1)
@@ -356,7 +402,7 @@ def main():
         "eager": {"ms_per_step": round(eager_ms_per_step, 5),
                   "value": round(set_bytes / (eager_ms_per_step * 1e-3) / 1e9, 1)},
         "roofline": roofline, "per_kernel": per_kernel, "gemm_m2048": gemm,
-        "fused_gate_up": fused, "cpu_baseline": cpu,
+        "fused_gate_up": fused, "hadamard": had, "cpu_baseline": cpu,
         "kernel_sources_sha256_16": khash,
     }
     print(json.dumps(out), flush=True)

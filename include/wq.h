@@ -187,6 +187,24 @@ wq_status wq_gemm_gate_up(const void* x, wq_dtype dt, const void* packed, wq_qmo
                           const uint16_t* lut, const int32_t* perm, void* y, int M, int N, int K,
                           int bits, int group_size, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * wq_hadamard -- online rotation of the activations before the product.  The
+ * FLUTE page lists Hadamard-transform support ("Maintenance & Community")
+ * without details; the reading: weights were rotated offline (H W) before
+ * quantisation, and each activation row is rotated at run time by the same
+ * orthonormal block-diagonal Walsh-Hadamard matrix H, so that (x H)(H W) = x W.
+ * For every row and every block of `block` consecutive elements starting at k0:
+ *     y[m][k0 + i] = block^(-1/2) * sum_j (-1)^popcount(i & j) * x[m][k0 + j]
+ * The rotated rows feed wq_gemv / wq_gemm (or the *_gate_up products) as x.
+ *   x, y  : device [M][K] in `dt`, 16-byte aligned; y == x rotates in place,
+ *           other overlaps are WQ_EINVAL
+ *   block : power of two, 2 <= block <= 512, K % block == 0 (else WQ_EINVAL);
+ *           K % 8 == 0 (else WQ_EUNSUPPORTED)
+ * fp32 arithmetic (fast Walsh-Hadamard butterflies), y rounded once to `dt`
+ * (RNE).  M == 0 is a valid no-op.
+ */
+wq_status wq_hadamard(const void* x, wq_dtype dt, void* y, int M, int K, int block, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

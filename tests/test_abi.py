@@ -30,7 +30,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for required in ("wq_repack", "wq_dequant_debug", "wq_gemv", "wq_gemm", "wq_packed_bytes",
                      "wq_workspace_bytes", "wq_status_str", "wq_layout_version",
-                     "wq_repack_gate_up", "wq_gemv_gate_up", "wq_gemm_gate_up"):
+                     "wq_repack_gate_up", "wq_gemv_gate_up", "wq_gemm_gate_up", "wq_hadamard"):
         assert required in names
 
 
@@ -135,3 +135,23 @@ def test_dequant_debug_rejects_before_launch(L):
     assert f(P(16), 0, None, None, 4096, 4096, 4, 128, 3, P(16), None) == 1   # bad out dtype
     assert f(P(16), 3, None, None, 4096, 4096, 4, 128, 0, P(16), None) == 1   # table missing
     assert f(None, 0, None, None, 4096, 4096, 4, 128, 0, P(16), None) == 1
+
+
+def test_hadamard_rejects_before_launch(L):
+    P = ctypes.c_void_p
+
+    def call(x=16, dt=0, y=4096, M=1, K=512, b=128):
+        return L.wq_hadamard(P(x) if x else None, dt, P(y) if y else None, M, K, b, None)
+
+    assert call(b=96) == 1            # not a power of two
+    assert call(b=1) == 1
+    assert call(b=1024) == 1          # larger than one wave holds
+    assert call(K=384, b=256) == 1    # K % block
+    assert call(dt=2) == 1
+    assert call(M=-1) == 1
+    assert call(x=0) == 1
+    assert call(y=0) == 1
+    assert call(x=8) == 2             # misaligned
+    assert call(K=4, b=2) == 2        # K % 8
+    assert call(y=16 + 256) == 1      # partial overlap
+    assert call(M=0) == 0             # empty: no-op

@@ -58,6 +58,8 @@ def lib() -> ctypes.CDLL:
             f = getattr(L, name)
             f.argtypes = [P, I, P, I, P, P, P, I, I, I, I, I, P, Z, P]
             f.restype = I
+        L.wq_hadamard.argtypes = [P, I, P, I, I, I, P]
+        L.wq_hadamard.restype = I
         if L.wq_layout_version() != LAYOUT_VERSION:
             raise RuntimeError("libwq.so layout version does not match this binding")
         _lib = L
@@ -164,7 +166,7 @@ def _product(fn: str, x: torch.Tensor, layer: PackedLayer, out: Optional[torch.T
     if x.dim() != 2 or x.shape[1] != layer.K or not x.is_contiguous():
         raise ValueError("x must be a contiguous [M][K] tensor")
     M = x.shape[0]
-    fused = fn.endswith("_gate_up")
+    fused = "_gate_up" in fn
     if fused != layer.gate_up:
         raise ValueError(f"{fn} needs a layer repacked by "
                          f"{'wq_repack_gate_up' if fused else 'wq_repack'}")
@@ -174,9 +176,8 @@ def _product(fn: str, x: torch.Tensor, layer: PackedLayer, out: Optional[torch.T
     if need and (ws is None or ws.numel() * ws.element_size() < need):
         ws = torch.empty(need, dtype=torch.uint8, device=x.device)
     rc = getattr(lib(), fn)(_ptr(x), _dt(x.dtype), _ptr(layer.packed), layer.mode, _ptr(layer.lut),
-                            _ptr(layer.perm), _ptr(out), M, layer.N, layer.K, layer.bits,
-                            layer.group_size, _ptr(ws) if need else None,
-                            need if need else 0, _stream(stream))
+                            _ptr(layer.perm), _ptr(out), M, layer.N, layer.K, layer.bits, layer.group_size,
+                            _ptr(ws) if need else None, need if need else 0, _stream(stream))
     _check(fn, rc)
     return out
 
@@ -199,6 +200,21 @@ def wq_gemv_gate_up(x: torch.Tensor, layer: PackedLayer, out=None, ws=None, stre
 def wq_gemm_gate_up(x: torch.Tensor, layer: PackedLayer, out=None, ws=None, stream=None) -> torch.Tensor:
     """h [M][N/2] = SiLU(x . gate) * (x . up) for any M."""
     return _product("wq_gemm_gate_up", x, layer, out, ws, stream)
+
+
+def wq_hadamard(x: torch.Tensor, block: int, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Rows of x [M][K] rotated by the orthonormal block-diagonal Walsh-Hadamard
+    matrix of size `block` (out may be x itself: in place)."""
+    if x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [M][K] tensor")
+    M, K = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    elif out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like x")
+    rc = lib().wq_hadamard(_ptr(x), _dt(x.dtype), _ptr(out), M, K, block, _stream(stream))
+    _check("wq_hadamard", rc)
+    return out
 
 
 def linear(x: torch.Tensor, layer: PackedLayer, out=None, ws=None, stream=None) -> torch.Tensor:

@@ -10,7 +10,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libwq.so")
 # (source, object name, extra defines): the kernel files are compiled once
 # per (activation dtype, code width) so the instantiations build in parallel.
-SOURCES = [("wq_api.hip", "wq_api", [])]
+SOURCES = [("wq_api.hip", "wq_api", []), ("wq_hadamard.hip", "wq_hadamard", [])]
 for _k in ("wq_gemv", "wq_gemm"):
     for _dt, _dn in ((0, "f16"), (1, "bf16")):
         for _b in (2, 3, 4):

@@ -376,4 +376,19 @@ wq_status wq_gemm_gate_up(const void* x, wq_dtype dt, const void* packed, wq_qmo
   return product(true, true, x, dt, packed, mode, lut, perm, y, M, N, K, bits, group_size, ws, ws_bytes, stream);
 }
 
+wq_status wq_hadamard(const void* x, wq_dtype dt, void* y, int M, int K, int block, void* stream) {
+  if (M < 0 || K <= 0) return WQ_EINVAL;
+  if (dt != WQ_F16 && dt != WQ_BF16) return WQ_EINVAL;
+  if (block < 2 || block > 512 || (block & (block - 1)) != 0 || K % block != 0) return WQ_EINVAL;
+  if (K % 8 != 0) return WQ_EUNSUPPORTED;
+  if ((size_t)M * K >= ((size_t)1 << 31)) return WQ_EUNSUPPORTED;
+  if (M == 0) return WQ_OK;
+  if (!x || !y) return WQ_EINVAL;
+  if (((uintptr_t)x | (uintptr_t)y) & 15) return WQ_EUNSUPPORTED;
+  // x and y either coincide (in place) or do not overlap
+  const uintptr_t xb = (uintptr_t)x, yb = (uintptr_t)y, n = (uintptr_t)M * K * 2;
+  if (xb != yb && xb < yb + n && yb < xb + n) return WQ_EINVAL;
+  return launch_hadamard(x, (int)dt, y, M, K, __builtin_ctz((unsigned)block), (hipStream_t)stream);
+}
+
 }  // extern "C"

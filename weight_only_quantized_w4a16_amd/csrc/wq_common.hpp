@@ -84,6 +84,9 @@ WQ_DECLARE_VARIANT(bf16_b4)
 #endif
 #endif
 
+// Online Hadamard rotation (validated arguments; lb = log2(block), 1..9).
+wq_status launch_hadamard(const void* x, int dt, void* y, int M, int K, int lb, hipStream_t s);
+
 inline wq_status launch_product(bool gemm, const ProductArgs& a) {
 #define WQ_PICK(v) return gemm ? launch_gemm_##v(a) : launch_gemv_##v(a)
   if (a.dt == F16) {

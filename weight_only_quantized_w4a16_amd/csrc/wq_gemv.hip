@@ -316,8 +316,10 @@ inline int pick_waves(int grid, int ktiles, int tn) {
 template <int DT, int BITS, int MODE, int TN, int GPU, bool PACKED, bool SWIGLU>
 wq_status run_pf(GemvArgs g, int grid, hipStream_t s) {
   const int tpw = g.kt_per_wave;
-  if (PACKED && tpw >= 8) return run<DT, BITS, MODE, TN, GPU, PACKED, 4, SWIGLU>(g, grid, s);
-  if (PACKED && tpw >= 5) return run<DT, BITS, MODE, TN, GPU, PACKED, 3, SWIGLU>(g, grid, s);
+  if constexpr (PACKED) {
+    if (tpw >= 8) return run<DT, BITS, MODE, TN, GPU, PACKED, 4, SWIGLU>(g, grid, s);
+    if (tpw >= 5) return run<DT, BITS, MODE, TN, GPU, PACKED, 3, SWIGLU>(g, grid, s);
+  }
   return run<DT, BITS, MODE, TN, GPU, PACKED, 2, SWIGLU>(g, grid, s);
 }
 
