@@ -25,6 +25,9 @@ Also reported:
                 entry points;
   hadamard      the online rotation of the activations alone and followed by
                 the product, on the QKV layer at M = 1 and 2048;
+  layer_stack   tokens per second through 32 LLaMA-7B-shaped decoder layers
+                (quantised products vs dense fp16 torch matmuls on weights
+                dequantised at load time), one HIP graph per token;
   cpu_baseline  the CPU oracle on a bounded sample of the same step.
 """
 import argparse
@@ -53,6 +56,9 @@ def parse():
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--no-fused", action="store_true")
     p.add_argument("--no-hadamard", action="store_true")
+    p.add_argument("--stack-layers", type=int, default=32,
+                   help="decoder layers in the token-by-token stack benchmark (0: skip it)")
+    p.add_argument("--stack-tokens", type=int, default=50)
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--copy-probe", action="store_true",
                    help="also run a plain device copy of known size (counter calibration)")
@@ -363,6 +369,86 @@ def main():
         del qp
         torch.cuda.empty_cache()
 
+    # ---------------- decode layer stack (tokens per second) ----------------
+    # A token through L LLaMA-7B-shaped decoder layers (fused QKV, o_proj,
+    # activation-fused gate+up, down; every layer its own weights, 107.5 MB
+    # per layer), captured as one HIP graph per token, against the same chain
+    # on weights dequantised at load time to dense fp16 and multiplied by
+    # torch (the exllama discussion's "dequantise at load" comparator).
+    stack = None
+    if args.stack_layers > 0:
+        from weight_only_quantized_w4a16_amd.stack import DecodeStack, DecoderWeights
+        nl = args.stack_layers
+        t_setup = time.perf_counter()
+        dec, dense = [], []
+        qbytes = 0
+        for li in range(nl):
+            ws = {}
+            dw = {}
+            for (name, _, _) in wl.LLAMA7B:
+                L = wl.stack_layer(li, name)
+                qbytes += L.weight_bytes()
+                pl = repack_copies(L, 1)[0]
+                dw[name] = wq.wq_dequant_debug(pl, torch.float16)
+                if name == "gate_up":
+                    pl = repack_copies(L, 1, wq.wq_repack_gate_up)[0]
+                ws[name] = pl
+            dec.append(DecoderWeights(ws["qkv"], ws["o_proj"], ws["gate_up"], ws["down"]))
+            dense.append(dw)
+        torch.cuda.synchronize()
+        setup_s = time.perf_counter() - t_setup
+        Ms = 1
+        st = DecodeStack(dec, Ms, torch.float16, dev)
+        dim, inter = st.dim, st.inter
+        x0 = to_dev(wl.make_x(Ms, dim, wl.F16, 4242), torch.float16)
+
+        def dense_step(x):
+            for dw in dense:
+                qkv = torch.matmul(x, dw["qkv"])
+                o = torch.matmul(qkv[:, :dim], dw["o_proj"])
+                gu = torch.matmul(o, dw["gate_up"])
+                h = torch.nn.functional.silu(gu[:, :inter]) * gu[:, inter:]
+                x = torch.matmul(h, dw["down"])
+            return x
+
+        def graph_time(fn):
+            cap = torch.cuda.Stream()
+            cap.wait_stream(stream)
+            with torch.cuda.stream(cap):
+                for _ in range(2):
+                    fn()
+            cap.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(cap):
+                with torch.cuda.graph(g, stream=cap):
+                    fn()
+            stream.wait_stream(cap)
+            torch.cuda.synchronize()
+            for _ in range(3):
+                g.replay()
+            torch.cuda.synchronize()
+            reps = max(5, args.stack_tokens)
+            e0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps, reps
+
+        q_ms, reps = graph_time(lambda: st.step(x0, stream=torch.cuda.current_stream()))
+        d_ms, _ = graph_time(lambda: dense_step(x0))
+        dbytes = sum(sum(t.numel() * 2 for t in dw.values()) for dw in dense)
+        stack = {"layers": nl, "M": Ms, "tokens_timed": reps, "setup_s": round(setup_s, 1),
+                 "quantized": {"ms_per_token": round(q_ms, 4), "tokens_per_s": round(1e3 / q_ms, 1),
+                               "weight_bytes_per_token": qbytes,
+                               "weight_GBps": round(qbytes / (q_ms * 1e-3) / 1e9, 1)},
+                 "dense_fp16_torch": {"ms_per_token": round(d_ms, 4), "tokens_per_s": round(1e3 / d_ms, 1),
+                                      "weight_bytes_per_token": dbytes,
+                                      "weight_GBps": round(dbytes / (d_ms * 1e-3) / 1e9, 1)},
+                 "speedup_vs_dense": round(d_ms / q_ms, 2)}
+        del dec, dense, st
+        torch.cuda.empty_cache()
+
     # ---------------- plain copy (counter calibration) ----------------
     if args.copy_probe:
         src = torch.empty(1 << 28, dtype=torch.uint8, device=dev).fill_(1)
@@ -402,7 +488,7 @@ def main():
         "eager": {"ms_per_step": round(eager_ms_per_step, 5),
                   "value": round(set_bytes / (eager_ms_per_step * 1e-3) / 1e9, 1)},
         "roofline": roofline, "per_kernel": per_kernel, "gemm_m2048": gemm,
-        "fused_gate_up": fused, "hadamard": had, "cpu_baseline": cpu,
+        "fused_gate_up": fused, "hadamard": had, "layer_stack": stack, "cpu_baseline": cpu,
         "kernel_sources_sha256_16": khash,
     }
     print(json.dumps(out), flush=True)

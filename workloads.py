@@ -199,3 +199,30 @@ CONFIGS = {
     # FLUTE page, "Limitations & Caveats": 4-bit, group 256, bf16 flagged unstable there.
     6: Config(6, "g256_regression", [("layer", 4096, 4096)], [1, 16, 2048], [4], [256], ZERO_F16, BF16, 5),
 }
+
+
+# ----------------------------------------------------------------------------
+# Decode layer stack: LLaMA-7B-shaped decoder layers chained token by token.
+# ----------------------------------------------------------------------------
+STACK_SEED = 11
+
+
+def stack_layer(li: int, lname: str) -> Layer:
+    """Linear layer `lname` of decoder layer `li` of the LLaMA-7B-shaped stack:
+    int4 codes, fp16 zero-points, group 128 (the decode configuration's
+    quantisation), fp16 activations.  Zero-points are U[5.5, 9.5], centred on
+    the mean code 7.5, so the weights have zero mean and no common-mode
+    component builds up from layer to layer.  Scales are U[0.5, 1.5] * c with
+    c = 1 / sqrt(E[U^2] * E[(q - z)^2] * K) (E[U^2] = 13/12,
+    E[(q - z)^2] = 21.25 + 4/3 for uniform codes and zero-points), so a
+    unit-variance input gives a unit-variance output; the down projection's c
+    is raised by 1 / sqrt(0.36), the mean square of SiLU(g) * u for unit normal
+    g and u, so activations keep their scale through any number of layers."""
+    K, N = next((k, n) for (nm, k, n) in LLAMA7B if nm == lname)
+    c = 1.0 / np.sqrt(13.0 / 12.0 * (21.25 + 4.0 / 3.0) * K)
+    if lname == "down":
+        c /= np.sqrt(0.36)
+    li_name = [nm for (nm, _, _) in LLAMA7B].index(lname)
+    seed = STACK_SEED * 1_000_003 + 1009 * li + li_name
+    return make_layer(K, N, 4, 128, ZERO_F16, seed, scale_range=(0.5 * c, 1.5 * c), zero_range=(5.5, 9.5),
+                      name=f"stack/{li}/{lname}")
