@@ -23,6 +23,7 @@ import numpy as np
 from . import build as _build
 
 SYM, ZERO_F16, ZERO_PACKED, LUT = 0, 1, 2, 3
+ZERO_F16_G8, ZERO_F16_G16, ZERO_F16_G32 = 4, 5, 6  # fp16 zero-points per 8 / 16 / 32 rows
 F16, BF16 = 0, 1
 
 _lib = None
@@ -131,7 +132,7 @@ def pack_zeros(z, bits):
 
 
 def _zeros_arr(mode, zeros):
-    if mode == ZERO_F16:
+    if mode in (ZERO_F16, ZERO_F16_G8, ZERO_F16_G16, ZERO_F16_G32):
         return _c(zeros, np.uint16)
     if mode == ZERO_PACKED:
         return _c(zeros, np.uint32)

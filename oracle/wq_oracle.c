@@ -20,7 +20,9 @@
  *   - a column-wise scale (group size -1) or group-wise scales (Triton GPTQ
  *     page, "Highlighted Details"; Marlin zero-point issue, efrantar);
  *   - act-order: the group of an input row is looked up in g_idx rather than
- *     derived from its index (Triton GPTQ page, "Limitations & Caveats").
+ *     derived from its index (Triton GPTQ page, "Limitations & Caveats");
+ *   - zero-points whose group size is chosen apart from the scales' (Marlin
+ *     zero-point issue, mobicham's reply, the HQQ+ experiment).
  *
  * Readings where the pages are silent (each listed in the design notes):
  *   canonical packing = per column, a little-endian bit stream along K (code
@@ -51,6 +53,14 @@
 #define WQO_ZERO_F16 1     /* fp16 zero-point per (group, column)         */
 #define WQO_ZERO_PACKED 2  /* bits-wide integer zero-point per (group, column) */
 #define WQO_LUT 3          /* w = s * T[q], fp16 table of 2^bits entries  */
+/* fp16 zero-points with a group of their own, 8 / 16 / 32 rows, decoupled from
+ * the scale group (Marlin zero-point issue, mobicham's reply: zero-point and
+ * scale group sizes chosen separately, e.g. per-column scales with a
+ * zero-point every 8 rows); zeros fp16 [K / zero group][N], indexed by the
+ * row's original position. */
+#define WQO_ZERO_F16_G8 4
+#define WQO_ZERO_F16_G16 5
+#define WQO_ZERO_F16_G32 6
 #define WQO_F16 0
 #define WQO_BF16 1
 
@@ -236,6 +246,8 @@ typedef struct {
   int K, N, bits, group_size, G, dtype;
 } layer_t;
 
+static int fine_zero_group(int mode);
+
 static int layer_check(const layer_t* L) {
   if (!L->qweight || !L->scales) return WQO_EINVAL;
   if (!bits_ok(L->bits) || L->K <= 0 || L->N <= 0) return WQO_EINVAL;
@@ -245,6 +257,11 @@ static int layer_check(const layer_t* L) {
   switch (L->mode) {
     case WQO_SYM: break;
     case WQO_ZERO_F16: if (!L->zeros) return WQO_EINVAL; break;
+    case WQO_ZERO_F16_G8:
+    case WQO_ZERO_F16_G16:
+    case WQO_ZERO_F16_G32:
+      if (!L->zeros || L->K % fine_zero_group(L->mode)) return WQO_EINVAL;
+      break;
     case WQO_ZERO_PACKED:
       if (!L->zeros || ((long)L->N * L->bits) % 32) return WQO_EINVAL;
       break;
@@ -255,6 +272,12 @@ static int layer_check(const layer_t* L) {
     for (int k = 0; k < L->K; ++k)
       if (L->g_idx[k] < 0 || L->g_idx[k] >= L->G) return WQO_EINVAL;
   return WQO_OK;
+}
+
+/* Rows per zero-point group of the modes whose zero-points have their own,
+ * finer group (0 for the other modes). */
+static int fine_zero_group(int mode) {
+  return mode == WQO_ZERO_F16_G8 ? 8 : mode == WQO_ZERO_F16_G16 ? 16 : mode == WQO_ZERO_F16_G32 ? 32 : 0;
 }
 
 static int group_of(const layer_t* L, int k) {
@@ -282,6 +305,9 @@ static uint16_t dequant_one(const layer_t* L, int k, int n) {
       z = (double)(1 << (L->bits - 1));
     } else if (L->mode == WQO_ZERO_F16) {
       z = wqo_f16_to_f64(((const uint16_t*)L->zeros)[(size_t)g * L->N + n]);
+    } else if (fine_zero_group(L->mode)) {
+      /* zero-point group of row k: k / zero-group rows (original row order) */
+      z = wqo_f16_to_f64(((const uint16_t*)L->zeros)[(size_t)(k / fine_zero_group(L->mode)) * L->N + n]);
     } else {
       size_t wpr = (size_t)L->N * L->bits / 32;
       z = (double)stream_code((const uint32_t*)L->zeros + (size_t)g * wpr, 1, n, L->bits);

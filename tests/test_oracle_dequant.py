@@ -76,6 +76,8 @@ def closed_form(L: wl.Layer, dtype: int) -> np.ndarray:
                     z = Fraction(1 << (b - 1))
                 elif L.mode == wl.ZERO_F16:
                     z = f16val(L.zeros[g, n])
+                elif L.mode in wl.FINE_ZERO_GROUP:
+                    z = f16val(L.zeros[k // wl.FINE_ZERO_GROUP[L.mode], n])
                 else:
                     z = Fraction(int(zc[g, n]))
                 e = s * (int(q[k, n]) - z)
@@ -89,7 +91,8 @@ def oracle_dequant(orc, L, dtype):
 
 
 CASES = [(mode, bits, dtype, gs, ao)
-         for mode in (wl.SYM, wl.ZERO_F16, wl.ZERO_PACKED, wl.LUT)
+         for mode in (wl.SYM, wl.ZERO_F16, wl.ZERO_PACKED, wl.LUT, wl.ZERO_F16_G8, wl.ZERO_F16_G16,
+                      wl.ZERO_F16_G32)
          for bits in (2, 3, 4)
          for dtype in (F16, BF16)
          for gs, ao in ((32, False), (-1, False), (32, True))]
@@ -102,6 +105,36 @@ def test_dequant_closed_form(orc, mode, bits, dtype, gs, ao):
     L = wl.make_layer(K, N, bits, gs, mode, seed, act_order=ao,
                       lut=wl.nf_table(bits) if mode == wl.LUT else None)
     assert np.array_equal(oracle_dequant(orc, L, dtype), closed_form(L, dtype))
+
+
+@pytest.mark.parametrize("fine", [wl.ZERO_F16_G8, wl.ZERO_F16_G16, wl.ZERO_F16_G32])
+@pytest.mark.parametrize("gs", [32, 64, -1])
+def test_fine_zero_groups_reduce_to_shared_groups(orc, fine, gs):
+    """Zero-points with their own group (Marlin zero-point issue, mobicham's
+    reply) that repeat the value of the scale group's zero-point give exactly
+    the fp16-zero mode with one zero-point per scale group."""
+    K, N = 128, 24
+    coarse = wl.make_layer(K, N, 4, gs, wl.ZERO_F16, 50 + gs % 7)
+    zg = wl.FINE_ZERO_GROUP[fine]
+    gsz = K if gs == -1 else gs
+    rows = np.arange(0, K, zg) // gsz  # scale group of each zero group
+    fine_layer = wl.Layer(K, N, 4, gs, fine, coarse.qweight, coarse.scales, coarse.zeros[rows])
+    for dt in (F16, BF16):
+        assert np.array_equal(oracle_dequant(orc, fine_layer, dt), oracle_dequant(orc, coarse, dt))
+
+
+def test_fine_zero_group_changes_within_a_scale_group(orc):
+    """One zero-point per 8 rows under a per-column scale: changing one
+    zero-point changes exactly its 8 rows of its column."""
+    K, N = 64, 8
+    L = wl.make_layer(K, N, 2, -1, wl.ZERO_F16_G8, 3)
+    base = oracle_dequant(orc, L, F16)
+    z2 = L.zeros.copy()
+    z2[3, 5] = wl.to_f16_bits(np.array([2.5]))[0]
+    L2 = wl.Layer(K, N, 2, -1, wl.ZERO_F16_G8, L.qweight, L.scales, z2)
+    diff = oracle_dequant(orc, L2, F16) != base
+    assert not diff[:, :5].any() and not diff[:, 6:].any()
+    assert not diff[:24, 5].any() and not diff[32:, 5].any()
 
 
 def test_dequant_subnormal_and_overflow_closed_form(orc):

@@ -28,7 +28,8 @@ def deq(orc, L, dtype):
 
 
 @pytest.mark.parametrize("mode,bits,dtype", [(wl.SYM, 4, F16), (wl.ZERO_F16, 3, F16),
-                                             (wl.ZERO_PACKED, 2, BF16), (wl.LUT, 4, BF16)])
+                                             (wl.ZERO_PACKED, 2, BF16), (wl.LUT, 4, BF16),
+                                             (wl.ZERO_F16_G8, 2, F16), (wl.ZERO_F16_G16, 3, BF16)])
 def test_brute_force_exact_sum(orc, mode, bits, dtype):
     M, K, N = 3, 64, 16
     L = wl.make_layer(K, N, bits, 32, mode, 7 + mode, lut=wl.nf_table(bits) if mode == wl.LUT else None)

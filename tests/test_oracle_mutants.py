@@ -46,6 +46,9 @@ MUTANTS = {
     "hadamard_or_for_and": ("  unsigned v = i & j;", "  unsigned v = i | j;"),
     "hadamard_norm": ("const double norm = 1.0 / sqrt((double)b);", "const double norm = 1.0 / (double)b;"),
     "hadamard_block_offset": ("const double* xb = x + (size_t)m * K + k0;", "const double* xb = x + (size_t)m * K;"),
+    "fine_zero_by_scale_group": ("z = wqo_f16_to_f64(((const uint16_t*)L->zeros)[(size_t)(k / fine_zero_group(L->mode)) * L->N + n]);",
+                                 "z = wqo_f16_to_f64(((const uint16_t*)L->zeros)[(size_t)g * L->N + n]);"),
+    "fine_zero_group_size": ("return mode == WQO_ZERO_F16_G8 ? 8 :", "return mode == WQO_ZERO_F16_G8 ? 16 :"),
     "bf16_as_f16": ("return dtype == WQO_BF16 ? wqo_f64_to_bf16(v) : wqo_f64_to_f16(v);",
                     "return wqo_f64_to_f16(v);"),
 }

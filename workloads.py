@@ -29,8 +29,12 @@ from typing import Optional
 import numpy as np
 
 SYM, ZERO_F16, ZERO_PACKED, LUT = 0, 1, 2, 3
+# fp16 zero-points in groups of 8 / 16 / 32 rows, independent of the scale group
+ZERO_F16_G8, ZERO_F16_G16, ZERO_F16_G32 = 4, 5, 6
+FINE_ZERO_GROUP = {ZERO_F16_G8: 8, ZERO_F16_G16: 16, ZERO_F16_G32: 32}
 F16, BF16 = 0, 1
-MODE_NAMES = {SYM: "sym", ZERO_F16: "zero_f16", ZERO_PACKED: "zero_packed", LUT: "lut"}
+MODE_NAMES = {SYM: "sym", ZERO_F16: "zero_f16", ZERO_PACKED: "zero_packed", LUT: "lut",
+              ZERO_F16_G8: "zero_f16_g8", ZERO_F16_G16: "zero_f16_g16", ZERO_F16_G32: "zero_f16_g32"}
 DTYPE_NAMES = {F16: "f16", BF16: "bf16"}
 
 
@@ -83,7 +87,8 @@ class Layer:
     mode: int
     qweight: np.ndarray                 # uint32 [K*bits/32][N]
     scales: np.ndarray                  # uint16 fp16 bits [G][N]
-    zeros: Optional[np.ndarray] = None  # uint16 [G][N] (fp16) or uint32 [G][N*bits/32]
+    zeros: Optional[np.ndarray] = None  # uint16 [G][N] (fp16), uint32 [G][N*bits/32], or
+                                        # uint16 [K/zg][N] (fp16, zero groups of zg rows)
     lut: Optional[np.ndarray] = None    # uint16 fp16 bits [2^bits]
     g_idx: Optional[np.ndarray] = None  # int32 [K]
     name: str = ""
@@ -117,6 +122,11 @@ def make_layer(K: int, N: int, bits: int, group_size: int, mode: int, seed: int,
     zeros = None
     if mode == ZERO_F16:
         zeros = to_f16_bits(rng.uniform(zero_range[0], zero_range[1], size=(G, N)))
+    elif mode in FINE_ZERO_GROUP:
+        zg = FINE_ZERO_GROUP[mode]
+        if K % zg:
+            raise ValueError("K must be a multiple of the zero group")
+        zeros = to_f16_bits(rng.uniform(zero_range[0], zero_range[1], size=(K // zg, N)))
     elif mode == ZERO_PACKED:
         if (N * bits) % 32:
             raise ValueError("N*bits must be a multiple of 32 for packed zero-points")
