@@ -25,6 +25,8 @@ Also reported:
                 entry points;
   hadamard      the online rotation of the activations alone and followed by
                 the product, on the QKV layer at M = 1 and 2048;
+  fine_zero_groups  2-bit layers with per-column scales and a zero-point per
+                8 rows, decode layer set shapes at M = 1 and 2048;
   layer_stack   tokens per second through 32 LLaMA-7B-shaped decoder layers
                 (quantised products vs dense fp16 torch matmuls on weights
                 dequantised at load time), one HIP graph per token;
@@ -56,6 +58,7 @@ def parse():
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--no-fused", action="store_true")
     p.add_argument("--no-hadamard", action="store_true")
+    p.add_argument("--no-fine", action="store_true")
     p.add_argument("--stack-layers", type=int, default=32,
                    help="decoder layers in the token-by-token stack benchmark (0: skip it)")
     p.add_argument("--stack-tokens", type=int, default=50)
@@ -124,7 +127,7 @@ def main():
         q = to_dev(L.qweight, torch.int32)
         s = to_dev(L.scales, torch.float16)
         z = None
-        if L.mode == wl.ZERO_F16:
+        if L.mode == wl.ZERO_F16 or L.mode in wl.FINE_ZERO_GROUP:
             z = to_dev(L.zeros, torch.float16)
         elif L.mode == wl.ZERO_PACKED:
             z = to_dev(L.zeros, torch.int32)
@@ -369,6 +372,44 @@ def main():
         del qp
         torch.cuda.empty_cache()
 
+    # ---------------- zero-points with their own group ----------------
+    # 2-bit codes, one scale per column and an fp16 zero-point every 8 rows
+    # (the zero-point granularity experiment of the Marlin zero-point issue),
+    # on the decode layer set's shapes: each layer at M = 1 (weight GB/s) and
+    # M = 2048 (TFLOP/s), launches back to back over rotated copies.
+    fine = None
+    if not args.no_fine:
+        fine = {"bits": 2, "group_size": -1, "zero_group": 8, "layers": {}}
+        for (name, K, N) in wl.LLAMA7B:
+            Lf = wl.make_layer(K, N, 2, -1, wl.ZERO_F16_G8, 8100 + K + N, scale_range=(0.002, 0.01),
+                               name=f"fine/{name}")
+            Rf = max(2, -(-(1 << 30) // Lf.weight_bytes()))
+            fp = repack_copies(Lf, Rf)
+            res = {"weight_bytes": Lf.weight_bytes()}
+            for Mf, fn in ((1, wq.wq_gemv), (2048, wq.wq_gemm)):
+                xf = to_dev(wl.make_x(Mf, K, wl.F16, 5), torch.float16)
+                yf = torch.empty((Mf, N), dtype=torch.float16, device=dev)
+                n = max(4 * Rf, 40) if Mf == 1 else Rf
+                for i in range(Rf):
+                    fn(xf, fp[i % Rf], out=yf, stream=stream)
+                torch.cuda.synchronize()
+                e0.record(stream)
+                for i in range(n):
+                    fn(xf, fp[i % Rf], out=yf, stream=stream)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) / n * 1e3
+                if Mf == 1:
+                    res["M1_us"] = round(us, 3)
+                    res["M1_weight_GBps"] = round(Lf.weight_bytes() / (us * 1e-6) / 1e9, 1)
+                else:
+                    res["M2048_us"] = round(us, 1)
+                    res["M2048_tflops"] = round(2.0 * Mf * N * K / (us * 1e-6) / 1e12, 1)
+                del xf, yf
+            fine["layers"][name] = res
+            del fp
+        torch.cuda.empty_cache()
+
     # ---------------- decode layer stack (tokens per second) ----------------
     # A token through L LLaMA-7B-shaped decoder layers (fused QKV, o_proj,
     # activation-fused gate+up, down; every layer its own weights, 107.5 MB
@@ -488,7 +529,7 @@ def main():
         "eager": {"ms_per_step": round(eager_ms_per_step, 5),
                   "value": round(set_bytes / (eager_ms_per_step * 1e-3) / 1e9, 1)},
         "roofline": roofline, "per_kernel": per_kernel, "gemm_m2048": gemm,
-        "fused_gate_up": fused, "hadamard": had, "layer_stack": stack, "cpu_baseline": cpu,
+        "fused_gate_up": fused, "hadamard": had, "fine_zero_groups": fine, "layer_stack": stack, "cpu_baseline": cpu,
         "kernel_sources_sha256_16": khash,
     }
     print(json.dumps(out), flush=True)

@@ -44,8 +44,9 @@
  *     K, code k at bit offset bits*k over qweight[0][n], qweight[1][n], ...
  *     (for 4 bits: word r holds rows 8r..8r+7, row 8r+i at bits 4i..4i+3);
  *   scales fp16 [G][N];
- *   zeros  fp16 [G][N] (WQ_ZERO_F16) or uint32 [G][N*bits/32] (WQ_ZERO_PACKED,
- *          row g a little-endian bit stream along N); NULL otherwise;
+ *   zeros  fp16 [G][N] (WQ_ZERO_F16), uint32 [G][N*bits/32] (WQ_ZERO_PACKED,
+ *          row g a little-endian bit stream along N), fp16 [K/zg][N]
+ *          (WQ_ZERO_F16_G8/16/32, zg = 8/16/32); NULL otherwise;
  *   g_idx  int32 [K] (act-order) or NULL.
  */
 #ifndef WQ_H
@@ -72,7 +73,16 @@ typedef enum {
   WQ_SYM = 0,           /* z = 2^(bits-1) */
   WQ_ZERO_F16 = 1,      /* fp16 zero-point per (group, column) */
   WQ_ZERO_PACKED = 2,   /* bits-wide integer zero-point per (group, column) */
-  WQ_LUT = 3            /* w = s * T[q], fp16 table of 2^bits entries */
+  WQ_LUT = 3,           /* w = s * T[q], fp16 table of 2^bits entries */
+  /* fp16 zero-points with a group of their own, 8 / 16 / 32 rows, apart from
+   * the scales' group_size (Marlin zero-point issue, mobicham's reply: the
+   * zero-point granularity matters most at low bit widths, e.g. per-column
+   * scales with a zero-point every 8 rows).  Row k of column n uses
+   * zeros[k / zg][n]; zeros fp16 [K / zg][N].  Not combinable with act-order
+   * (WQ_EUNSUPPORTED): the zero groups follow the original row order. */
+  WQ_ZERO_F16_G8 = 4,
+  WQ_ZERO_F16_G16 = 5,
+  WQ_ZERO_F16_G32 = 6
 } wq_qmode;
 
 /* Version of the repacked layout; a stored repacked buffer from another

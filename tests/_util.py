@@ -38,7 +38,7 @@ def repack_layer(wq, L: wl.Layer, device="cuda"):
     q = bits_to_tensor(L.qweight, torch.int32, device)
     s = bits_to_tensor(L.scales, torch.float16, device)
     z = None
-    if L.mode == wl.ZERO_F16:
+    if L.mode == wl.ZERO_F16 or L.mode in wl.FINE_ZERO_GROUP:
         z = bits_to_tensor(L.zeros, torch.float16, device)
     elif L.mode == wl.ZERO_PACKED:
         z = bits_to_tensor(L.zeros, torch.int32, device)

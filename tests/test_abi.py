@@ -54,6 +54,10 @@ def test_packed_bytes_matches_layout(L):
     assert L.wq_packed_bytes(K, N, 4, 128, 1) == al(al(codes) + 32 * N * 4)  # (scale, zero) pairs
     assert L.wq_packed_bytes(K, N, 4, 32, 2) == al(al(al(codes) + 128 * N * 2) + 128 * (N // 16) * 8)
     assert L.wq_packed_bytes(K, N, 3, -1, 3) == al(al(K * N * 3 // 8) + N * 2)
+    # fine zero-points: 8 * (32 / zg) bytes per column per 128 rows
+    for mode, zg in ((4, 8), (5, 16), (6, 32)):
+        assert L.wq_packed_bytes(K, N, 2, -1, mode) == al(al(al(K * N // 4) + N * 2) + K * N * 2 // zg)
+    assert L.wq_packed_bytes(K, N, 4, 128, 7) == 0   # no such mode
     # unsupported / invalid -> 0
     assert L.wq_packed_bytes(4096, 4104, 4, 128, 0) == 0   # N % 16
     assert L.wq_packed_bytes(4000, 4096, 4, 128, 0) == 0   # K % 128

@@ -16,6 +16,7 @@ from typing import Optional
 import torch
 
 SYM, ZERO_F16, ZERO_PACKED, LUT = 0, 1, 2, 3
+ZERO_F16_G8, ZERO_F16_G16, ZERO_F16_G32 = 4, 5, 6  # fp16 zero-points per 8 / 16 / 32 rows
 F16, BF16 = 0, 1
 LAYOUT_VERSION = 2
 
@@ -138,8 +139,8 @@ def wq_repack(qweight: torch.Tensor, scales: torch.Tensor, zeros: Optional[torch
               g_idx, K: int, N: int, bits: int, group_size: int, lut: Optional[torch.Tensor] = None,
               stream=None) -> PackedLayer:
     """Canonical GPTQ-style tensors (device: qweight int32 [K*bits/32][N], scales fp16
-    [G][N], zeros fp16 [G][N] or int32 [G][N*bits/32]) -> PackedLayer.  g_idx: host
-    int32 array-like [K] or None."""
+    [G][N], zeros fp16 [G][N], int32 [G][N*bits/32] or fp16 [K/zg][N] for the fine
+    zero-point modes) -> PackedLayer.  g_idx: host int32 array-like [K] or None."""
     return _repack("wq_repack", qweight, scales, zeros, mode, g_idx, K, N, bits, group_size, lut, stream)
 
 

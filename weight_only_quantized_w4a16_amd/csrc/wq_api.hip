@@ -114,6 +114,22 @@ __global__ void repack_zeros_packed_kernel(const uint32_t* __restrict__ zp, int 
   dst[i] = word;
 }
 
+// Fine zero-points: fp16 [K / zg][N] -> [N/16][K/128][16][HC][4] (layout in
+// wq_layout.hpp).  One thread per entry.
+__global__ void repack_zeros_fine_kernel(const uint16_t* __restrict__ zeros, int N, int K, int zg, int ntiles,
+                                         int gate_up, uint16_t* __restrict__ dst) {
+  const int hcs = 32 / zg;  // row classes per k-block
+  const size_t total = (size_t)ntiles * (K / 128) * 16 * hcs * 4;
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const int kb = (int)(i % 4), hc = (int)((i / 4) % hcs), c = (int)((i / (4 * hcs)) % 16);
+  const size_t rest = i / (64 * hcs);
+  const int u = (int)(rest % (K / 128)), nt = (int)(rest / (K / 128));
+  const int h0 = hc * 4 / hcs;  // first lane row block of the class
+  const int row = 128 * u + 32 * kb + 8 * h0;
+  dst[i] = zeros[(size_t)(row / zg) * N + source_tile(nt, ntiles, gate_up) * 16 + c];
+}
+
 // ---------------------------------------------------------------------------
 // Debug dequantisation: one wave per tile, exact path (the one the large-M
 // product uses), written back in the original row order.
@@ -149,7 +165,12 @@ __global__ __launch_bounds__(64) void dequant_debug_kernel(const uint8_t* __rest
     const int j = L.gpu > 1 ? (row0 % 128) / L.gsz : 0;  // group inside the record
     const size_t ri = (((size_t)nt * L.nrec + rec) * 16 + c) * L.gpu + j;
     float sv, zv;
-    if (MODE == ZERO_F16) {
+    if (MODE == ZFINE) {
+      sv = f16_to_f32(((const uint16_t*)S)[ri]);
+      const int zg = fine_zero_group(L.mode), hcs = 32 / zg;
+      const size_t zi = ((((size_t)nt * (L.K / 128) + unit) * 16 + c) * hcs + h * hcs / 4) * 4 + (row0 % 128) / 32;
+      zv = f16_to_f32(((const uint16_t*)Z)[zi]);
+    } else if (MODE == ZERO_F16) {
       const uint32_t w2 = ((const uint32_t*)S)[ri];
       sv = f16_to_f32((uint16_t)(w2 & 0xFFFFu));
       zv = f16_to_f32((uint16_t)(w2 >> 16));
@@ -219,9 +240,11 @@ static wq_status repack(const uint32_t* qweight, const uint16_t* scales, const v
   if (st != WQ_OK) return st;
   if (gate_up && N % 32 != 0) return WQ_EUNSUPPORTED;
   if (!qweight || !scales || !packed) return WQ_EINVAL;
-  if ((mode == ZERO_F16 || mode == ZERO_PACKED) && !zeros) return WQ_EINVAL;
+  if ((mode == ZERO_F16 || mode == ZERO_PACKED || fine_zero_group(mode)) && !zeros) return WQ_EINVAL;
   if (mode == ZERO_PACKED && ((long)N * bits) % 32 != 0) return WQ_EINVAL;
   if (g_idx_host && !perm) return WQ_EINVAL;
+  // fine zero groups follow the original row order, which act-order breaks up
+  if (g_idx_host && fine_zero_group(mode)) return WQ_EUNSUPPORTED;
   const Layout L = make_layout(K, N, bits, group_size, mode);
   hipStream_t s = (hipStream_t)stream;
 
@@ -261,6 +284,12 @@ static wq_status repack(const uint32_t* qweight, const uint16_t* scales, const v
   hipLaunchKernelGGL(repack_scales_kernel, dim3(L.nrec, L.ntiles), dim3(16 * L.gpu), 0, s, scales,
                      mode == ZERO_F16 ? (const uint16_t*)zeros : nullptr, N, L.nrec, L.gpu, gate_up,
                      (void*)(out + L.scales_off));
+  if (fine_zero_group(mode)) {
+    const size_t n = L.zeros_bytes / 2;
+    hipLaunchKernelGGL(repack_zeros_fine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       (const uint16_t*)zeros, N, K, fine_zero_group(mode), L.ntiles, gate_up,
+                       (uint16_t*)(out + L.zeros_off));
+  }
   if (mode == ZERO_PACKED) {
     const int words = L.ntiles * L.nrec * 2 * L.gpu;
     dim3 g2((words + 255) / 256);
@@ -298,6 +327,7 @@ wq_status wq_dequant_debug(const void* packed, wq_qmode mode, const uint16_t* lu
   if (!packed || !w) return WQ_EINVAL;
   if (out != WQ_F16 && out != WQ_BF16) return WQ_EINVAL;
   if (mode == LUT && !lut) return WQ_EINVAL;
+  if (perm && fine_zero_group(mode)) return WQ_EUNSUPPORTED;
   const Layout L = make_layout(K, N, bits, group_size, mode);
   hipStream_t s = (hipStream_t)stream;
   dim3 grid(L.ktiles, L.ntiles);
@@ -308,9 +338,9 @@ wq_status wq_dequant_debug(const void* packed, wq_qmode mode, const uint16_t* lu
     sfor<2>([&](auto di) {
       constexpr int D = decltype(di)::value;
       if (D != (int)out) return;
-      sfor<4>([&](auto mi) {
+      sfor<5>([&](auto mi) {
         constexpr int MODE = decltype(mi)::value;
-        if (MODE != (int)mode) return;
+        if (MODE != kernel_mode((int)mode)) return;
         hipLaunchKernelGGL((dequant_debug_kernel<B, D, MODE>), grid, dim3(64), 0, s, (const uint8_t*)packed, L,
                            lut, perm, (uint16_t*)w);
         launched = true;
@@ -333,6 +363,7 @@ static wq_status product(bool gemm, bool swiglu, const void* x, wq_dtype dt, con
   if (M == 0) return WQ_OK;
   if (!x || !packed || !y) return WQ_EINVAL;
   if (mode == LUT && !lut) return WQ_EINVAL;
+  if (perm && fine_zero_group(mode)) return WQ_EUNSUPPORTED;
   if (((uintptr_t)x | (uintptr_t)y | (uintptr_t)packed) & 15) return WQ_EUNSUPPORTED;
   if (M > (1 << 24)) return WQ_EUNSUPPORTED;
   if ((size_t)M * K * 2 >= ((size_t)1 << 31)) return WQ_EUNSUPPORTED;  // activation buffer offsets

@@ -24,7 +24,7 @@ __host__ __device__ inline void sfor(F&& f) {
 inline wq_status check_layer(int K, int N, int bits, int group_size, int mode) {
   if (K <= 0 || N <= 0) return WQ_EINVAL;
   if (bits != 2 && bits != 3 && bits != 4) return WQ_EINVAL;
-  if (mode < SYM || mode > LUT) return WQ_EINVAL;
+  if (mode < SYM || mode > ZFINE32) return WQ_EINVAL;
   if (group_size != -1 && (group_size <= 0 || K % group_size != 0)) return WQ_EINVAL;
   if (K > (1 << 24) || N > (1 << 24)) return WQ_EUNSUPPORTED;
   if (N % 16 != 0 || K % tile_k(bits) != 0) return WQ_EUNSUPPORTED;

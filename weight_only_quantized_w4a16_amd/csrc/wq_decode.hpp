@@ -227,6 +227,35 @@ __device__ inline u32x4 biased_frag(const uint32_t* w, const DecodeConsts& k) {
   return r;
 }
 
+// Fine zero-points, scale applied later: B operand RN_dt(q - z) for k-block KB,
+// whose eight rows share one zero-point z (fp16 bits zbits).
+//   fp16: (1024 + q) - 1024 is exact, one packed add of -z rounds once;
+//   bf16: (128 + q) widened to fp32, minus (128 + z) (exact: both fit 24
+//         bits), one rounding to bf16.
+template <int BITS, int DT, int KB>
+__device__ inline u32x4 fine_frag(const uint32_t* w, uint32_t zbits, const DecodeConsts& k) {
+  const u32x4 o = biased_frag<BITS, KB>(w, k);
+  u32x4 r;
+  if constexpr (DT == F16) {
+    const _Float16 z = __builtin_bit_cast(_Float16, (uint16_t)zbits);
+    const h2 nz = h2{-z, -z};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r[q] = as_u32((as_h2(o[q]) + h2s(-1024.0f)) + nz);
+  } else {
+    const float cz = 128.0f + f16_to_f32((uint16_t)zbits);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      r[q] = pack2<BF16>(__uint_as_float(o[q] << 16) - cz, __uint_as_float(o[q] & 0xFFFF0000u) - cz);
+  }
+  return r;
+}
+
+// fp16 bits of the zero-point of k-block kbu (0..3) from a fine zero record
+// (two words, four fp16 values, k-block order).
+__device__ inline uint32_t fine_zero_bits(const uint32_t* zr, int kbu) {
+  return (zr[kbu >> 1] >> (16 * (kbu & 1))) & 0xFFFFu;
+}
+
 // ---------------------------------------------------------------------------
 // Table decode: B operand from an LDS pair table.  tab points at the table's
 // column for this lane (base + (lane % 32)); entry idx sits at tab[idx * 32].
@@ -299,6 +328,7 @@ struct ExactParams {
   float s;        // scale
   float sz;       // s * z (exact in fp32)
   h2 s_h;         // scale as an fp16 pair (fp16 fast paths)
+  h2 nz_h;        // fp16 product path: -z (fp16 zero-points) or -(1024 + z) (integer zero-points)
 };
 
 // Exact dequantised B operand for k-block KB: RN_dt(s*(q - z)) or RN_dt(s*T[q]).
@@ -334,6 +364,33 @@ __device__ inline u32x4 exact_frag(const uint32_t* w, const ExactParams& p, cons
       r[q] = pack2<DT>(__builtin_fmaf(c[2 * q], p.s, -p.sz), __builtin_fmaf(c[2 * q + 1], p.s, -p.sz));
   }
   return r;
+}
+
+// B operand of the large-M product for k-block KB.  With fp16 activations and
+// stored zero-points the subtraction and the scale run as packed fp16
+// arithmetic on the biased codes (1024 + q):
+//   integer zero-points: (1024 + q) - (1024 + z) is exact, then one rounding
+//     of s * (q - z): exactly RN(s * (q - z));
+//   fp16 zero-points: q - z is formed in fp16 (exact unless it needs more than
+//     11 significant bits) and then scaled: RN(s * RN(q - z)), at most one
+//     extra rounding away from RN(s * (q - z));
+// every other case takes the exact decode above.
+template <int BITS, int DT, int MODE, int KB>
+__device__ inline u32x4 product_frag(const uint32_t* w, const ExactParams& p, const uint32_t* tab,
+                                     const DecodeConsts& k) {
+  if constexpr (DT == F16 && (MODE == ZERO_F16 || MODE == ZFINE || MODE == ZERO_PACKED)) {
+    const u32x4 o = biased_frag<BITS, KB>(w, k);
+    u32x4 r;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      h2 d = as_h2(o[q]);
+      if constexpr (MODE != ZERO_PACKED) d = d + h2s(-1024.0f);
+      r[q] = as_u32((d + p.nz_h) * p.s_h);
+    }
+    return r;
+  } else {
+    return exact_frag<BITS, DT, MODE, KB>(w, p, tab, k);
+  }
 }
 
 // ---------------------------------------------------------------------------

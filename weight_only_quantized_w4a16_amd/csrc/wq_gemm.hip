@@ -41,6 +41,7 @@ struct GemmArgs {
   uint32_t codes_bytes, s_bytes, z_bytes;
   int M, N, K, nrec, upr, ktiles, ntiles, mtiles, ntiles_wg;  // upr: 128-row units per metadata record
   int swiglu;             // fused gate+up layer: y [M][N/2] = SiLU(gate) * up
+  int zg;                 // rows per fine zero-point group (fine mode only)
 };
 
 // s_waitcnt immediate (gfx9 encoding) that waits until at most n vector
@@ -61,7 +62,8 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
   constexpr int REC = (Z16 ? 4 : 2) * GPU;   // scale record bytes per column
   constexpr int SW = REC < 4 ? 1 : REC / 4;  // words per scale record
   constexpr int ZREC = 4 * GPU;              // packed-zero record bytes per column half
-  constexpr int ZW = MODE == ZERO_PACKED ? GPU : 1;
+  constexpr bool FINE = MODE == ZFINE;       // fp16 zero-point per k-block row block
+  constexpr int ZW = MODE == ZERO_PACKED ? GPU : FINE ? 2 : 1;
   constexpr int AW = BM / 16;         // 1-KiB activation loads per wave per unit
 
   __shared__ uint32_t table[TABLE ? (32 << (2 * BITS)) : 1];
@@ -89,7 +91,11 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
   const rsrc_t rx = make_rsrc(a.x, (uint32_t)a.M * a.K * 2);
   const rsrc_t rc = make_rsrc(a.codes, a.codes_bytes);
   const rsrc_t rs = make_rsrc(a.S, a.s_bytes);
-  const rsrc_t rz = make_rsrc(MODE == ZERO_PACKED ? a.Z : a.S, MODE == ZERO_PACKED ? a.z_bytes : 0u);
+  const rsrc_t rz = make_rsrc(MODE == ZERO_PACKED || FINE ? a.Z : a.S, MODE == ZERO_PACKED || FINE ? a.z_bytes : 0u);
+  // fine zero records: 8 * hcs bytes per column and 128-row unit, this lane's row class at 8 hc
+  const int hcs = FINE ? 32 / a.zg : 1;
+  const uint32_t zf_rec = 8u * hcs;
+  const uint32_t zf_lane = (uint32_t)c * zf_rec + 8u * ((h * hcs) >> 2);
 
   if constexpr (TABLE) fill_pair_table<BITS, false>(table, a.lut, tid, 256);
   const uint32_t* tab = table + (lane & 31);
@@ -120,7 +126,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
     const int nt = min(nt0 + t, a.ntiles - 1);
     b_voff[t] = (uint32_t)(nt * a.ktiles * 64 + lane) * WPL * 4;
     s_soff_t[t] = (uint32_t)(nt * a.nrec) * 16 * REC;
-    z_soff_t[t] = (uint32_t)(nt * a.nrec) * 2 * ZREC;
+    z_soff_t[t] = FINE ? (uint32_t)(nt * a.ktiles * UPT) * 16u * zf_rec : (uint32_t)(nt * a.nrec) * 2 * ZREC;
   }
   // Weight registers of one tile.
   struct BSet {
@@ -129,7 +135,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
     uint32_t z[UPT][NT][ZW];
   };
   // loads issued by one b_load (codes, scale records, packed-zero records)
-  constexpr int NBL = NT * (1 + (EPI_SCALE ? 0 : UPT) + (MODE == ZERO_PACKED ? UPT : 0));
+  constexpr int NBL = NT * (1 + (EPI_SCALE ? 0 : UPT) + (MODE == ZERO_PACKED || FINE ? UPT : 0));
   auto b_load = [&](BSet& bs, int kt) {
     // Past K every offset gets 2^31 added (out of range, reads zero): a
     // scalar add instead of a select, so the code stays branch-free.
@@ -158,6 +164,8 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
           load_record<REC>(rs, (uint32_t)c * REC + oob, s_soff_t[t] + rec * 16 * REC, bs.s[u][t]);
           if constexpr (MODE == ZERO_PACKED)
             load_record<ZREC>(rz, (uint32_t)(c >> 3) * ZREC + oob, z_soff_t[t] + rec * 2 * ZREC, bs.z[u][t]);
+          if constexpr (FINE)
+            load_record<8>(rz, zf_lane + oob, z_soff_t[t] + (uint32_t)(ktc * UPT + u) * 16u * zf_rec, bs.z[u][t]);
         }
       }
     }
@@ -187,6 +195,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
           prm[t].s = sv;
           prm[t].s_h = h2s(sv);
           prm[t].sz = MODE == LUT ? 0.0f : sv * z;
+          prm[t].nz_h = h2s(MODE == ZERO_PACKED ? -(1024.0f + z) : -z);
         }
       }
       sfor<KBPG>([&](auto kc) {
@@ -195,10 +204,18 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
         u32x4 bf[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-          if constexpr (EPI_SCALE)
+          if constexpr (EPI_SCALE) {
             bf[t] = offset_frag<BITS, DT, kb>(cw[t], dk);
-          else
-            bf[t] = exact_frag<BITS, DT, MODE, kb>(cw[t], prm[t], tab, dk);
+          } else if constexpr (FINE) {
+            // the k-block's own zero-point
+            ExactParams pk = prm[t];
+            const float zk = f16_to_f32((uint16_t)fine_zero_bits(cz[t], kbu));
+            pk.sz = pk.s * zk;
+            pk.nz_h = h2s(-zk);
+            bf[t] = product_frag<BITS, DT, MODE, kb>(cw[t], pk, tab, dk);
+          } else {
+            bf[t] = product_frag<BITS, DT, MODE, kb>(cw[t], prm[t], tab, dk);
+          }
         }
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
@@ -313,15 +330,21 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
 
 template <int DT, int BITS, int MODE, int GPU, bool EPI>
 wq_status run_gemm(GemmArgs g, hipStream_t s) {
-  // 128-row tiles unless that leaves fewer than about two workgroups per CU
+  // 128-row tiles unless that leaves fewer than about two workgroups per CU.
+  // Modes whose decode needs more registers (fp16 zero-points, tables) run
+  // 64-row tiles: at 128 rows they spill (or drop to one wave per SIMD), which
+  // measured slower than decoding each weight for half as many rows.
+  constexpr bool HEAVY = MODE == ZERO_F16 || MODE == LUT || MODE == ZFINE;
   g.ntiles_wg = (g.N + 255) / 256;
-  const int bm = (g.M <= 64 || (long)((g.M + 127) / 128) * g.ntiles_wg < 480) ? 64 : 128;
+  const int bm = (HEAVY || g.M <= 64 || (long)((g.M + 127) / 128) * g.ntiles_wg < 480) ? 64 : 128;
   g.mtiles = (g.M + bm - 1) / bm;
   const int grid = g.mtiles * g.ntiles_wg;
-  if (bm == 64)
+  if (bm == 64) {
     hipLaunchKernelGGL((gemm_kernel<DT, BITS, MODE, GPU, EPI, 64>), dim3(grid), dim3(256), 0, s, g);
-  else
-    hipLaunchKernelGGL((gemm_kernel<DT, BITS, MODE, GPU, EPI, 128>), dim3(grid), dim3(256), 0, s, g);
+  } else {
+    if constexpr (!HEAVY)
+      hipLaunchKernelGGL((gemm_kernel<DT, BITS, MODE, GPU, EPI, 128>), dim3(grid), dim3(256), 0, s, g);
+  }
   return launch_status();
 }
 
@@ -345,12 +368,13 @@ wq_status WQ_CAT(launch_gemm_, WQ_VARIANT)(const ProductArgs& p) {
   g.ktiles = L.ktiles; g.ntiles = L.ntiles;
   g.mtiles = 0; g.ntiles_wg = 0;
   g.swiglu = p.swiglu;
+  g.zg = fine_zero_group(p.mode);
   const int gpu = L.gsz >= 128 ? 1 : 128 / L.gsz;
   const bool epi = L.G == 1 && p.mode == SYM && D == F16;
   wq_status st = WQ_EINVAL;
-  sfor<4>([&](auto mi) {
+  sfor<5>([&](auto mi) {
     constexpr int MODE = decltype(mi)::value;
-    if (MODE != p.mode) return;
+    if (MODE != kernel_mode(p.mode)) return;
     if (gpu == 1) {
       if (epi) { if constexpr (MODE == SYM && D == F16) st = run_gemm<D, B, MODE, 1, true>(g, p.stream); }
       else st = run_gemm<D, B, MODE, 1, false>(g, p.stream);

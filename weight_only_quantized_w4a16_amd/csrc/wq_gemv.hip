@@ -42,15 +42,29 @@ struct GemvArgs {
   uint32_t codes_bytes, s_bytes, z_bytes;
   int M, N, K, nrec, upr, ktiles, waves, kt_per_wave;  // upr: 128-row units per metadata record
   int ldy;                // row stride of y (N, or N / 2 for a fused gate+up layer)
+  int zg;                 // rows per fine zero-point group (8, 16, 32; fine mode only)
 };
 
-// Decode k-block KB of a tile into a B operand.
+// Decode k-block KB of a tile into a B operand (fine mode only: zbits is the
+// k-block's zero-point, s its scale).  Fine zero-points with fp16 activations
+// give RN(q - z) (11 bits, the scale comes after the MFMA); with bf16
+// activations RN(q - z) would keep only 8 bits, so the weight is the
+// dequantised RN(s * (q - z)) itself and no scale follows.
 template <int BITS, int DT, int MODE, int KB>
-__device__ inline u32x4 decode_frag(const uint32_t* w, const uint32_t* tab, const DecodeConsts& k) {
-  if constexpr (MODE == LUT)
+__device__ inline u32x4 decode_frag(const uint32_t* w, const uint32_t* tab, const DecodeConsts& k, uint32_t zbits,
+                                    float s) {
+  if constexpr (MODE == LUT) {
     return table_frag<BITS, KB>(w, tab);
-  else
+  } else if constexpr (MODE == ZFINE && DT == BF16) {
+    ExactParams p;
+    p.s = s;
+    p.sz = s * f16_to_f32((uint16_t)zbits);
+    return exact_frag<BITS, DT, MODE, KB>(w, p, tab, k);
+  } else if constexpr (MODE == ZFINE) {
+    return fine_frag<BITS, DT, KB>(w, zbits, k);
+  } else {
     return biased_frag<BITS, KB>(w, k);
+  }
 }
 
 // Zero-point correction c for (group, column): B - c == q - z (see biased_frag).
@@ -73,11 +87,14 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const GemvArgs a) {
   constexpr int KBPG = 4 / GPU;                 // k-blocks per group inside a unit
   constexpr bool TABLE = MODE == LUT;
   constexpr bool Z16 = MODE == ZERO_F16;
-  constexpr bool HAS_Z = MODE == ZERO_F16 || MODE == ZERO_PACKED;
+  constexpr bool FINE = MODE == ZFINE;          // fine zero-points: B = q - z, scale after
+  constexpr bool HAS_Z = MODE == ZERO_F16 || MODE == ZERO_PACKED || FINE;
   constexpr int REC = (Z16 ? 4 : 2) * GPU;      // scale record bytes per column
   constexpr int SW = REC < 4 ? 1 : REC / 4;     // words per scale record
   constexpr int ZREC = 4 * GPU;                 // packed-zero record bytes per column half
-  constexpr bool XS = MODE != LUT;              // uniform modes remove bias + z via row sums
+  constexpr bool XS = MODE != LUT && !FINE;     // shared zero-points: remove bias + z via row sums
+  constexpr bool SCALED = FINE && DT == BF16;   // decoded weights already carry the scale
+  constexpr int ZW = FINE ? 2 : (HAS_Z && !Z16 ? GPU : 1);  // words of a zero record
   constexpr int NRED = PACKED ? 1 : 4;          // reduced values per lane per column tile
 
   __shared__ uint32_t table[TABLE ? (32 << (2 * BITS)) : 1];
@@ -103,6 +120,11 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const GemvArgs a) {
   const uint32_t w_lane = (uint32_t)lane * WPL * 4;
   const uint32_t s_lane = (uint32_t)c * REC;
   const uint32_t zp_lane = (uint32_t)(c >> 3) * ZREC;
+  // fine zero records: 8 * hcs bytes per column and unit, this lane's class at 8 hc
+  const int hcs = FINE ? 32 / a.zg : 1;
+  const uint32_t zf_rec = 8u * hcs;
+  const uint32_t zf_lane = (uint32_t)c * zf_rec + 8u * ((h * hcs) >> 2);
+  const int nunits = a.ktiles * UPT;
 
   const int kt0 = kslot * a.kt_per_wave;
   const int kt1 = min(kt0 + a.kt_per_wave, a.ktiles);
@@ -111,7 +133,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const GemvArgs a) {
     uint32_t w[TN][WPL];
     u32x4 xa[NXA];
     uint32_t s[TN][UPT][SW];                  // scale record (with fp16 zero-points when Z16)
-    uint32_t z[TN][UPT][HAS_Z && !Z16 ? GPU : 1];  // packed-zero record
+    uint32_t z[TN][UPT][ZW];                  // packed or fine zero-point record
   };
 
   // Loads of tile kt (all of them out of range, hence free, when kt >= kt1).
@@ -147,6 +169,9 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const GemvArgs a) {
         load_record<REC>(rs, ok ? s_lane : kOutOfRange, ri * 16 * REC, f.s[t][u]);
         if constexpr (MODE == ZERO_PACKED)
           load_record<ZREC>(rz, ok ? zp_lane : kOutOfRange, ri * 2 * ZREC, f.z[t][u]);
+        if constexpr (FINE)
+          load_record<8>(rz, ok ? zf_lane : kOutOfRange,
+                         (uint32_t)((nt0 + t) * nunits + ktc * UPT + u) * 16u * zf_rec, f.z[t][u]);
       }
     }
   };
@@ -186,7 +211,9 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const GemvArgs a) {
           constexpr int kb = decltype(kbc)::value;
 #pragma unroll
           for (int t = 0; t < TN; ++t) {
-            const u32x4 b = decode_frag<BITS, DT, MODE, 4 * u + kb>(f.w[t], tab, dk);
+            const u32x4 b = decode_frag<BITS, DT, MODE, 4 * u + kb>(
+                f.w[t], tab, dk, FINE ? fine_zero_bits(f.z[t][u], kb) : 0u,
+                SCALED ? rec_scale<Z16>(f.s[t][u], kb / KBPG) : 0.0f);
             acc[t][kb] = mfma16<DT>(f.xa[u], b, zero4);
           }
         });
@@ -198,7 +225,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const GemvArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int j = e / KBPG;
-            const float s = rec_scale<Z16>(f.s[t][u], j);
+            const float s = SCALED ? 1.0f : rec_scale<Z16>(f.s[t][u], j);
             float v = acc[t][e][e];
             if constexpr (XS) v = __builtin_fmaf(-zero_corr<DT>(zero_of(f, t, u, j)), xs[e], v);
             tot[t][e] = __builtin_fmaf(s, v, tot[t][e]);
@@ -215,14 +242,16 @@ __global__ __launch_bounds__(1024) void gemv_kernel(const GemvArgs a) {
             constexpr int kb = 4 * u + gi * KBPG + decltype(kc)::value;  // k-block inside the tile
 #pragma unroll
             for (int t = 0; t < TN; ++t) {
-              const u32x4 b = decode_frag<BITS, DT, MODE, kb>(f.w[t], tab, dk);
+              const u32x4 b = decode_frag<BITS, DT, MODE, kb>(
+                  f.w[t], tab, dk, FINE ? fine_zero_bits(f.z[t][u], kb - 4 * u) : 0u,
+                  SCALED ? rec_scale<Z16>(f.s[t][u], gi) : 0.0f);
               acc[t] = mfma16<DT>(f.xa[kb], b, acc[t]);
             }
             if constexpr (XS) xs = mfma16<DT>(f.xa[kb], ones_frag<DT>(), xs);
           });
 #pragma unroll
           for (int t = 0; t < TN; ++t) {
-            const float s = rec_scale<Z16>(f.s[t][u], gi);
+            const float s = SCALED ? 1.0f : rec_scale<Z16>(f.s[t][u], gi);
             const float cz = XS ? zero_corr<DT>(zero_of(f, t, u, gi)) : 0.0f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -375,11 +404,12 @@ wq_status WQ_CAT(launch_gemv_, WQ_VARIANT)(const ProductArgs& p) {
   g.ktiles = L.ktiles;
   g.waves = 1; g.kt_per_wave = 0;
   g.ldy = p.swiglu ? p.N / 2 : p.N;
+  g.zg = fine_zero_group(p.mode);
   const int gpu = L.gsz >= 128 ? 1 : 128 / L.gsz;  // groups per 128-row unit
   wq_status st = WQ_EINVAL;
-  sfor<4>([&](auto mi) {
+  sfor<5>([&](auto mi) {
     constexpr int MODE = decltype(mi)::value;
-    if (MODE != p.mode) return;
+    if (MODE != kernel_mode(p.mode)) return;
     if (p.swiglu) {
       if (gpu == 1) st = pick_shape<D, B, MODE, 1, true>(g, p.stream);
       else if (gpu == 2) st = pick_shape<D, B, MODE, 2, true>(g, p.stream);

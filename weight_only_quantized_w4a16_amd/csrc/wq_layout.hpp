@@ -36,6 +36,15 @@
 //                   zero-points of columns 8h..8h+7 of group j as nibbles
 //                   (whatever the code width).
 // Record r covers unit r when groups are smaller than 128 rows, else group r.
+//
+// Fine zero-points (zero groups of ZG = 8, 16 or 32 rows, apart from the
+// scale groups): fp16 [N/16][K/128][16][HC][4] with HC = 32 / ZG row classes.
+// Lane (c, h) of a wave needs, for k-block kb of a 128-row unit, the zero of
+// rows 32 kb + 8 h .. + 7 (one zero group); lanes h with the same class
+// hc = h * HC / 4 share it.  Entry [nt][u][c][hc][kb] is that zero, so a lane
+// reads its four (one per k-block) with one 8-byte load at
+// ((nt * K/128 + u) * 16 + c) * 8 HC + 8 hc.  Scales then use the symmetric
+// mode's records.
 #pragma once
 #include <stddef.h>
 #include <stdint.h>
@@ -44,7 +53,11 @@
 
 namespace wq {
 
-enum { SYM = 0, ZERO_F16 = 1, ZERO_PACKED = 2, LUT = 3 };
+// Modes of the C ABI; 4..6 are fp16 zero-points per 8 / 16 / 32 rows, which
+// the kernels handle as one mode (ZFINE) with the zero group as a value.
+enum { SYM = 0, ZERO_F16 = 1, ZERO_PACKED = 2, LUT = 3, ZFINE = 4, ZFINE16 = 5, ZFINE32 = 6 };
+WQ_HD int fine_zero_group(int mode) { return mode == ZFINE ? 8 : mode == ZFINE16 ? 16 : mode == ZFINE32 ? 32 : 0; }
+WQ_HD int kernel_mode(int mode) { return mode >= ZFINE ? ZFINE : mode; }
 enum { F16 = 0, BF16 = 1 };
 
 WQ_HD int tile_k(int bits) { return bits == 2 ? 256 : 128; }
@@ -90,6 +103,7 @@ inline Layout make_layout(int K, int N, int bits, int group_size, int mode) {
   L.scales_bytes = (size_t)L.ntiles * L.nrec * 16 * L.rec_bytes;
   L.zeros_off = align256(L.scales_off + L.scales_bytes);
   L.zeros_bytes = mode == ZERO_PACKED ? (size_t)L.ntiles * L.nrec * 2 * L.gpu * 4 : 0;
+  if (fine_zero_group(mode)) L.zeros_bytes = (size_t)L.ntiles * (K / 128) * 16 * (256 / fine_zero_group(mode));
   L.total = align256(L.zeros_off + L.zeros_bytes);
   return L;
 }
