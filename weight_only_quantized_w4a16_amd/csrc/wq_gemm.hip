@@ -178,30 +178,50 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
     for (int t = 0; t < NT; ++t) acc[i][t] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 
   // One 128-row unit of K from stage `As`: 4 k-blocks of MT x NT MFMAs.
+  // A fragment (activation rows 16 i .. 16 i + 15, k-block kbu) from stage As.
+  auto a_frag = [&](const u32x4* As, int kbu, int i) {
+    const int r = 16 * i + c;
+    return As[r * 16 + ((4 * kbu + h) ^ (r & 15))];
+  };
+  // One 128-row unit of K from stage `As`: 4 k-blocks of MT x NT MFMAs, taken
+  // as pairs of row subtiles.  With 128-row tiles the A fragments of the next
+  // pair are read from LDS before the MFMAs of the current pair are issued, so
+  // each read has a whole pair of MFMAs (8 x NT) to complete; with 64-row
+  // tiles the extra registers would cost a wave per SIMD, so the reads stay
+  // next to their MFMAs.
+  constexpr bool LOOKAHEAD = BM == 128;
   auto compute_unit = [&](const u32x4* As, const uint32_t (&cw)[NT][WPL], const uint32_t (&cs)[NT][SW],
                           const uint32_t (&cz)[NT][ZW], auto uc) {
     constexpr int u = decltype(uc)::value;
-    sfor<GPU>([&](auto gc) {
-      constexpr int gi = decltype(gc)::value;
-      ExactParams prm[NT];
-      if constexpr (!EPI_SCALE) {
+    constexpr int PAIRS = MT / 2;       // row-subtile pairs per k-block
+    constexpr int STEPS = 4 * PAIRS;    // pairs per unit
+    ExactParams prm[NT];
+    u32x4 bf[NT];
+    u32x4 f0, f1;
+    if constexpr (LOOKAHEAD) {
+      f0 = a_frag(As, 0, 0);
+      f1 = a_frag(As, 0, 1);
+    }
+    sfor<STEPS>([&](auto sc) {
+      constexpr int step = decltype(sc)::value;
+      constexpr int kbu = step / PAIRS, ip = step % PAIRS;  // k-block inside the unit, pair
+      constexpr int kb = 4 * u + kbu;                         // k-block inside the tile
+      constexpr int gi = kbu / KBPG;                          // group inside the unit
+      if constexpr (ip == 0) {
+        if constexpr (!EPI_SCALE && kbu % KBPG == 0) {
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const float sv = rec_scale<Z16>(cs[t], gi);
-          float z;
-          if constexpr (MODE == ZERO_F16) z = rec_zero16(cs[t], gi);
-          else if constexpr (MODE == ZERO_PACKED) z = rec_zero_packed(cz[t], gi, c);
-          else z = (float)(1 << (BITS - 1));
-          prm[t].s = sv;
-          prm[t].s_h = h2s(sv);
-          prm[t].sz = MODE == LUT ? 0.0f : sv * z;
-          prm[t].nz_h = h2s(MODE == ZERO_PACKED ? -(1024.0f + z) : -z);
+          for (int t = 0; t < NT; ++t) {
+            const float sv = rec_scale<Z16>(cs[t], gi);
+            float z;
+            if constexpr (MODE == ZERO_F16) z = rec_zero16(cs[t], gi);
+            else if constexpr (MODE == ZERO_PACKED) z = rec_zero_packed(cz[t], gi, c);
+            else z = (float)(1 << (BITS - 1));
+            prm[t].s = sv;
+            prm[t].s_h = h2s(sv);
+            prm[t].sz = MODE == LUT ? 0.0f : sv * z;
+            prm[t].nz_h = h2s(MODE == ZERO_PACKED ? -(1024.0f + z) : -z);
+          }
         }
-      }
-      sfor<KBPG>([&](auto kc) {
-        constexpr int kbu = gi * KBPG + decltype(kc)::value;  // k-block inside the unit
-        constexpr int kb = 4 * u + kbu;                        // k-block inside the tile
-        u32x4 bf[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           if constexpr (EPI_SCALE) {
@@ -217,14 +237,25 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
             bf[t] = product_frag<BITS, DT, MODE, kb>(cw[t], prm[t], tab, dk);
           }
         }
-#pragma unroll
-        for (int i = 0; i < MT; ++i) {
-          const int r = 16 * i + c;
-          const u32x4 af = As[r * 16 + ((4 * kbu + h) ^ (r & 15))];
-#pragma unroll
-          for (int t = 0; t < NT; ++t) acc[i][t] = mfma16<DT>(bf[t], af, acc[i][t]);
+      }
+      u32x4 n0 = f0, n1 = f1;
+      if constexpr (!LOOKAHEAD) {
+        f0 = a_frag(As, kbu, 2 * ip);
+        f1 = a_frag(As, kbu, 2 * ip + 1);
+      } else {
+        if constexpr (step + 1 < STEPS) {
+          constexpr int nk = (step + 1) / PAIRS, ni = 2 * ((step + 1) % PAIRS);
+          n0 = a_frag(As, nk, ni);
+          n1 = a_frag(As, nk, ni + 1);
         }
-      });
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[2 * ip][t] = mfma16<DT>(bf[t], f0, acc[2 * ip][t]);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[2 * ip + 1][t] = mfma16<DT>(bf[t], f1, acc[2 * ip + 1][t]);
+      f0 = n0;
+      f1 = n1;
     });
   };
 
