@@ -66,8 +66,18 @@ def test_packed_bytes_matches_layout(L):
 
 
 def test_workspace_bytes(L):
-    assert L.wq_workspace_bytes(16, 4096, 4096, 4, 0) == 0
-    assert L.wq_workspace_bytes(16, 4096, 4096, 4, 1) == 16 * 4096 * 2
+    al = lambda v: (v + 255) // 256 * 256
+    assert L.wq_workspace_bytes(128, 4096, 4096, 4, 0) == 0          # M > 64: no K split
+    assert L.wq_workspace_bytes(128, 4096, 4096, 4, 1) == al(128 * 4096 * 2)
+    assert L.wq_workspace_bytes(65, 53248, 16384, 4, 0) == 0
+    # narrow problems split K: 16 workgroups of 256 columns -> 32 slices wanted,
+    # capped at 4 k-tiles per slice (32 k-tiles -> 8 slices)
+    assert L.wq_workspace_bytes(16, 4096, 4096, 4, 0) == 8 * 16 * 4096 * 4
+    assert L.wq_workspace_bytes(16, 4096, 4096, 4, 1) == al(16 * 4096 * 2) + 8 * 16 * 4096 * 4
+    # 208 workgroups -> 3 slices of 43 (last 42) k-tiles
+    assert L.wq_workspace_bytes(32, 53248, 16384, 4, 0) == 3 * 32 * 53248 * 4
+    # wide enough: no split
+    assert L.wq_workspace_bytes(64, 131072, 4096, 4, 0) == 0
 
 
 def call_product(L, fn, M=1, N=4096, K=4096, bits=4, gs=128, mode=0, dt=0, x=16, w=16, y=16, lut=None,

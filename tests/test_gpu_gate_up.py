@@ -136,6 +136,17 @@ def test_gemm_gate_up_parity(orc, wq, mode, bits, dt, gs, M, ao):
     check_gate_up(orc, wq, "wq_gemm_gate_up", L, M, dt, 41 + M)
 
 
+@pytest.mark.parametrize("mode,dt", [(wl.SYM, wl.F16), (wl.ZERO_F16, wl.BF16), (wl.LUT, wl.F16)])
+def test_gemm_gate_up_k_split(orc, wq, mode, dt):
+    """A narrow fused gate+up layer at small M splits K; the reduction kernel
+    applies SiLU(gate) * up to the summed halves."""
+    K, N = 2048, 448
+    for gs in (128, -1):
+        for M in (1, 33):
+            L = make(mode, 4, gs, K, N, 7500 + mode + dt + M)
+            check_gate_up(orc, wq, "wq_gemm_gate_up", L, M, dt, 77 + M)
+
+
 def test_gate_up_m_zero_and_layer_kind(wq):
     L = make(wl.SYM, 4, 128, 512, 64, 5)
     fused = repack_gate_up(wq, L)

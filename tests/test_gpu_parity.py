@@ -161,3 +161,29 @@ def test_group256_bf16_regression(orc, wq):
         L = make(mode, 4, 256, 4096, 256, 9)
         for fn, M in (("wq_gemv", 1), ("wq_gemv", 16), ("wq_gemm", 256)):
             check_product(orc, wq, fn, L, M, wl.BF16, 11 + M)
+
+
+KSPLIT_CASES = [(mode, bits, dt, gs) for mode in MODES for bits in (2, 4) for dt in (wl.F16, wl.BF16)
+                for gs in (128, -1)]
+
+
+@pytest.mark.parametrize("mode,bits,dt,gs", KSPLIT_CASES)
+def test_gemm_k_split_parity(orc, wq, mode, bits, dt, gs):
+    """Narrow large-M products split K over several workgroups (fp32 partial
+    sums in the workspace, summed by a second kernel): 224 columns and
+    K = 2048 give 4 slices, for M = 1, 17, 64 and the last slice ragged."""
+    K, N = 2048, 224
+    assert wq.wq_workspace_bytes(64, N, K, bits, False) > 0
+    for M in (1, 17, 64):
+        print(f"[gemm k-split] mode={mode} bits={bits} dt={dt} gs={gs} M={M}", flush=True)
+        L = make(mode, bits, gs, K, N, 8000 + 97 * mode + 13 * bits + 5 * dt + M)
+        check_product(orc, wq, "wq_gemm", L, M, dt, 123 + M)
+
+
+def test_gemm_k_split_uneven_and_act_order(orc, wq):
+    """K = 1664 (13 k-tiles) splits into slices of 4, 4, 4 and 1 tiles; with
+    act-order the workspace holds the permuted activations and the partial
+    sums side by side."""
+    L = make(wl.ZERO_PACKED, 4, 128, 1664, 96, 77, act_order=True)
+    for M in (3, 40):
+        check_product(orc, wq, "wq_gemm", L, M, wl.BF16, 9 + M)

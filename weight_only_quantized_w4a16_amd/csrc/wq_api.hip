@@ -227,10 +227,18 @@ size_t wq_packed_bytes(int K, int N, int bits, int group_size, wq_qmode mode) {
   return make_layout(K, N, bits, group_size, mode).total;
 }
 
+// Workspace layout: [permuted x, M*K*2 bytes, when act-order] then, 256-byte
+// aligned, [K-split partial products, ksplit*M*N*4 bytes, large-M product
+// only].
+static size_t perm_ws_bytes(int M, int K, int has_perm) { return has_perm ? align256((size_t)M * K * 2) : 0; }
+static size_t split_ws_bytes(int M, int N, int K, int bits) {
+  const int ks = gemm_ksplit(M, N, K, bits);
+  return ks > 1 ? (size_t)ks * M * N * 4 : 0;
+}
+
 size_t wq_workspace_bytes(int M, int N, int K, int bits, int has_perm) {
-  (void)N; (void)bits;
-  if (M <= 0 || K <= 0 || !has_perm) return 0;
-  return (size_t)M * K * 2;
+  if (M <= 0 || K <= 0 || N <= 0) return 0;
+  return perm_ws_bytes(M, K, has_perm) + split_ws_bytes(M, N, K, bits);
 }
 
 static wq_status repack(const uint32_t* qweight, const uint16_t* scales, const void* zeros, wq_qmode mode,
@@ -367,7 +375,8 @@ static wq_status product(bool gemm, bool swiglu, const void* x, wq_dtype dt, con
   if (((uintptr_t)x | (uintptr_t)y | (uintptr_t)packed) & 15) return WQ_EUNSUPPORTED;
   if (M > (1 << 24)) return WQ_EUNSUPPORTED;
   if ((size_t)M * K * 2 >= ((size_t)1 << 31)) return WQ_EUNSUPPORTED;  // activation buffer offsets
-  const size_t need = wq_workspace_bytes(M, N, K, bits, perm != nullptr);
+  const int ksplit = gemm ? gemm_ksplit(M, N, K, bits) : 1;
+  const size_t need = perm_ws_bytes(M, K, perm != nullptr) + (ksplit > 1 ? split_ws_bytes(M, N, K, bits) : 0);
   if (need && (!ws || ws_bytes < need)) return WQ_ENOSPACE;
   if (need && ((uintptr_t)ws & 15)) return WQ_EUNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
@@ -380,6 +389,8 @@ static wq_status product(bool gemm, bool swiglu, const void* x, wq_dtype dt, con
     xin = ws;
   }
   ProductArgs a{xin, (int)dt, packed, (int)mode, lut, y, M, N, K, bits, group_size, swiglu ? 1 : 0, s};
+  a.ksplit = ksplit;
+  a.part = ksplit > 1 ? (void*)((uint8_t*)ws + perm_ws_bytes(M, K, perm != nullptr)) : nullptr;
   return launch_product(gemm, a);
 }
 

@@ -38,6 +38,21 @@ inline wq_status check_layer(int K, int N, int bits, int group_size, int mode) {
   return WQ_OK;
 }
 
+// K split of the large-M product.  Workgroups cover 256 columns and (for
+// M <= 64) all rows, so a narrow layer leaves most of the GPU idle; its K range
+// is then split until about 512 workgroups run, keeping at least 4 k-tiles per
+// split.  The partial products go through an fp32 workspace.
+inline int gemm_ksplit(int M, int N, int K, int bits) {
+  if (M > 64) return 1;
+  const int nwg = (N + 255) / 256;
+  const int ktiles = K / tile_k(bits);
+  int s = (512 + nwg - 1) / nwg;
+  if (s > ktiles / 4) s = ktiles / 4;
+  if (s <= 1) return 1;
+  const int per = (ktiles + s - 1) / s;  // k-tiles per split; no split left empty
+  return (ktiles + per - 1) / per;
+}
+
 inline wq_status launch_status() {
   return hipGetLastError() == hipSuccess ? WQ_OK : WQ_EHIP;
 }
@@ -53,6 +68,8 @@ struct ProductArgs {
   int M, N, K, bits, group_size;
   int swiglu;               // 1: fused gate+up layer, y [M][N/2] = SiLU(gate) * up
   hipStream_t stream;
+  int ksplit = 1;           // GEMM only: K split over this many workgroups
+  void* part = nullptr;     // ksplit > 1: fp32 workspace [ksplit][M][N]
 };
 #define WQ_CAT2(a, b) a##b
 #define WQ_CAT(a, b) WQ_CAT2(a, b)

@@ -42,6 +42,8 @@ struct GemmArgs {
   int M, N, K, nrec, upr, ktiles, ntiles, mtiles, ntiles_wg;  // upr: 128-row units per metadata record
   int swiglu;             // fused gate+up layer: y [M][N/2] = SiLU(gate) * up
   int zg;                 // rows per fine zero-point group (fine mode only)
+  int ksplit, ktps;       // K split over ksplit workgroups of ktps k-tiles (1: no split)
+  float* part;            // ksplit > 1: fp32 partial products [ksplit][M][N]
 };
 
 // s_waitcnt immediate (gfx9 encoding) that waits until at most n vector
@@ -84,7 +86,8 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
   // tiles (which stay in its L2) while the weight column blocks stream past,
   // each shared by the XCD's workgroups on the same block.
   const int bid = blockIdx.x;
-  const int mt = bid % a.mtiles, nb = bid / a.mtiles;
+  const int mt = bid % a.mtiles, nb = (bid / a.mtiles) % a.ntiles_wg, ks = bid / (a.mtiles * a.ntiles_wg);
+  const int kt0 = ks * a.ktps, kt1 = min(kt0 + a.ktps, a.ktiles);  // this workgroup's k-tiles
   const int m0 = mt * BM;
   const int nt0 = nb * (BN / 16) + wave * NT;  // first 16-column tile of this wave
 
@@ -139,7 +142,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
   auto b_load = [&](BSet& bs, int kt) {
     // Past K every offset gets 2^31 added (out of range, reads zero): a
     // scalar add instead of a select, so the code stays branch-free.
-    const bool ok = kt < a.ktiles;
+    const bool ok = kt < kt1;
     const int ktc = ok ? kt : 0;
     const uint32_t oob = ok ? 0u : kOutOfRange;
     const uint32_t kofs = (uint32_t)ktc * 64 * WPL * 4 + oob;
@@ -267,11 +270,11 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
   // weights keep streaming.  The compiler's wait tracking does not see the
   // LDS-destination loads, hence the explicit waits; a scheduling barrier
   // keeps the two groups of loads in program order.
-  const int nunits = a.ktiles * UPT;
+  const int uend = kt1 * UPT;  // first unit past this workgroup's range
   BSet set0, set1;
-  a_issue(0, As0);
-  b_load(set0, 0);
-  b_load(set1, 1);
+  a_issue(kt0 * UPT, As0);
+  b_load(set0, kt0);
+  b_load(set1, kt0 + 1);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();
 
@@ -281,12 +284,12 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
       constexpr int u = decltype(uc)::value;
       const int unit = kt * UPT + u;
       // the stage of a unit alternates; with UPT = 2 it follows u, else kt
-      const bool odd = UPT == 2 ? (u == 1) : (kt & 1);
-      if (unit + 1 < nunits) a_issue(unit + 1, odd ? As0 : As1);
+      const bool odd = UPT == 2 ? (u == 1) : ((kt - kt0) & 1);
+      if (unit + 1 < uend) a_issue(unit + 1, odd ? As0 : As1);
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (u == 0) b_load(cur, kt + 2);
       compute_unit(odd ? As1 : As0, use.w, use.s[u], use.z[u], uc);
-      if (unit + 1 < nunits) {
+      if (unit + 1 < uend) {
         // u == 0: the weight loads issued after the activation loads may stay
         // in flight; later units have no newer loads
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(u == 0 ? NBL : 0));
@@ -294,9 +297,9 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
       }
     });
   };
-  for (int kt = 0; kt < a.ktiles; kt += 2) {
+  for (int kt = kt0; kt < kt1; kt += 2) {
     tile(kt, set0);
-    if (kt + 1 < a.ktiles) tile(kt + 1, set1);
+    if (kt + 1 < kt1) tile(kt + 1, set1);
   }
 
   // ---- epilogue.  The MFMAs take the weights as the A operand and the
@@ -314,6 +317,27 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
     }
   };
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  if (a.ksplit > 1) {
+    // Split K: this workgroup's fp32 partial sums (scaled when the scale sits
+    // in the epilogue) go to its slice of the workspace; the reduction kernel
+    // adds the slices in split order and applies the output stage.
+    float* dst = a.part + (size_t)ks * a.M * a.N;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (nt0 + t >= a.ntiles) continue;
+      const int n = (nt0 + t) * 16 + 4 * h;
+      float s[4];
+      col_scales(t, s);
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        const int m = m0 + 16 * i + c;
+        if (m < a.M)
+          *(f4*)(dst + (size_t)m * a.N + n) =
+              f4{acc[i][t][0] * s[0], acc[i][t][1] * s[1], acc[i][t][2] * s[2], acc[i][t][3] * s[3]};
+      }
+    }
+    return;
+  }
   if (a.swiglu) {
     // Fused gate+up layer: column tiles are interleaved (gate, up, ...), so
     // tiles 2p and 2p + 1 of the wave are the gate and up halves of output
@@ -359,6 +383,35 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
   }
 }
 
+// Sum of the K-split partial products, in split order, rounded once to the
+// activation dtype (y [M][N]), or, for a fused gate+up layer, SiLU(gate) * up
+// of the summed halves (y [M][N/2]; partial columns in the interleaved tile
+// order).  One thread per 4 consecutive outputs.
+template <int DT>
+__global__ __launch_bounds__(256) void ksplit_reduce_kernel(const float* __restrict__ part, int ksplit, int M, int N,
+                                                            int swiglu, uint16_t* __restrict__ y) {
+  const int ldy = swiglu ? N / 2 : N;
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (size_t)M * ldy / 4) return;
+  const int m = (int)(i * 4 / ldy), j = (int)(i * 4 % ldy);  // first of 4 outputs (ldy % 16 == 0)
+  const size_t slice = (size_t)M * N;
+  f4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (!swiglu) {
+    for (int k = 0; k < ksplit; ++k) v += *(const f4*)(part + k * slice + (size_t)m * N + j);
+  } else {
+    const int col = (j / 16) * 32 + j % 16;  // gate column of output j; its up column is 16 further
+    f4 g = v, u = v;
+    for (int k = 0; k < ksplit; ++k) {
+      g += *(const f4*)(part + k * slice + (size_t)m * N + col);
+      u += *(const f4*)(part + k * slice + (size_t)m * N + col + 16);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = g[e] / (1.0f + expf(-g[e])) * u[e];
+  }
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  *(u32x2*)(y + (size_t)m * ldy + j) = u32x2{pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
+}
+
 template <int DT, int BITS, int MODE, int GPU, bool EPI>
 wq_status run_gemm(GemmArgs g, hipStream_t s) {
   // 128-row tiles unless that leaves fewer than about two workgroups per CU.
@@ -369,12 +422,18 @@ wq_status run_gemm(GemmArgs g, hipStream_t s) {
   g.ntiles_wg = (g.N + 255) / 256;
   const int bm = (HEAVY || g.M <= 64 || (long)((g.M + 127) / 128) * g.ntiles_wg < 480) ? 64 : 128;
   g.mtiles = (g.M + bm - 1) / bm;
-  const int grid = g.mtiles * g.ntiles_wg;
+  g.ktps = (g.ktiles + g.ksplit - 1) / g.ksplit;
+  const int grid = g.mtiles * g.ntiles_wg * g.ksplit;
   if (bm == 64) {
     hipLaunchKernelGGL((gemm_kernel<DT, BITS, MODE, GPU, EPI, 64>), dim3(grid), dim3(256), 0, s, g);
   } else {
     if constexpr (!HEAVY)
       hipLaunchKernelGGL((gemm_kernel<DT, BITS, MODE, GPU, EPI, 128>), dim3(grid), dim3(256), 0, s, g);
+  }
+  if (g.ksplit > 1) {
+    const size_t quads = (size_t)g.M * (g.swiglu ? g.N / 2 : g.N) / 4;
+    hipLaunchKernelGGL((ksplit_reduce_kernel<DT>), dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, s,
+                       (const float*)g.part, g.ksplit, g.M, g.N, g.swiglu, g.y);
   }
   return launch_status();
 }
@@ -400,6 +459,9 @@ wq_status WQ_CAT(launch_gemm_, WQ_VARIANT)(const ProductArgs& p) {
   g.mtiles = 0; g.ntiles_wg = 0;
   g.swiglu = p.swiglu;
   g.zg = fine_zero_group(p.mode);
+  g.ksplit = p.ksplit;
+  g.part = (float*)p.part;
+  g.ktps = L.ktiles;
   const int gpu = L.gsz >= 128 ? 1 : 128 / L.gsz;
   const bool epi = L.G == 1 && p.mode == SYM && D == F16;
   wq_status st = WQ_EINVAL;
