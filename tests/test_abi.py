@@ -169,3 +169,14 @@ def test_hadamard_rejects_before_launch(L):
     assert call(K=4, b=2) == 2        # K % 8
     assert call(y=16 + 256) == 1      # partial overlap
     assert call(M=0) == 0             # empty: no-op
+
+
+def test_size_limits(L):
+    """Every section of a repacked layer stays below 2 GiB (32-bit buffer
+    offsets) and K, N below 2^24: larger layers are rejected up front."""
+    assert L.wq_packed_bytes(65536, 65536, 4, 128, 0) == 0        # 2 GiB of codes
+    assert L.wq_packed_bytes(65536, 65520, 4, 128, 0) > 0         # just below
+    assert L.wq_packed_bytes(1 << 25, 16, 4, 128, 0) == 0         # K past 2^24
+    assert call_product(L, "wq_gemv", K=65536, N=65536) == 2
+    # activations: M*K*2 bytes must stay below 2 GiB
+    assert call_product(L, "wq_gemm", M=1 << 18, K=4096) == 2

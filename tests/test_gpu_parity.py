@@ -187,3 +187,31 @@ def test_gemm_k_split_uneven_and_act_order(orc, wq):
     L = make(wl.ZERO_PACKED, 4, 128, 1664, 96, 77, act_order=True)
     for M in (3, 40):
         check_product(orc, wq, "wq_gemm", L, M, wl.BF16, 9 + M)
+
+
+@pytest.mark.parametrize("fn,M", [("wq_gemv", 1), ("wq_gemv", 16), ("wq_gemm", 1), ("wq_gemm", 17)])
+def test_smallest_layer(orc, wq, fn, M):
+    """One tile: K = 128 rows, N = 16 columns (one workgroup, one k-tile)."""
+    for mode in MODES:
+        L = make(mode, 4, 32, 128, 16, 60 + mode)
+        check_product(orc, wq, fn, L, M, wl.F16, 7 + M)
+
+
+@pytest.mark.parametrize("fn,M", [("wq_gemv", 3), ("wq_gemm", 40), ("wq_gemm", 300)])
+def test_degenerate_values(orc, wq, fn, M):
+    """Zero scales give zero output; zero activations give zero output; equal
+    activation rows give equal output rows; group = K matches group -1 bit for bit."""
+    K, N = 1024, 64
+    L = make(wl.ZERO_F16, 4, 128, K, N, 3)
+    L0 = wl.Layer(K, N, 4, 128, wl.ZERO_F16, L.qweight, np.zeros_like(L.scales), L.zeros)
+    x_bits = wl.make_x(M, K, wl.F16, 4)
+    x = bits_to_tensor(x_bits, torch.float16, "cuda")
+    assert torch.count_nonzero(getattr(wq, fn)(x, repack_layer(wq, L0))) == 0
+    assert torch.count_nonzero(getattr(wq, fn)(torch.zeros_like(x), repack_layer(wq, L))) == 0
+    xr = x[:1].repeat(M, 1).contiguous()
+    y = getattr(wq, fn)(xr, repack_layer(wq, L))
+    assert torch.equal(y, y[:1].expand(M, N))
+    Lg = wl.make_layer(K, N, 4, -1, wl.SYM, 8)
+    LK = wl.Layer(K, N, 4, K, wl.SYM, Lg.qweight, Lg.scales)
+    assert torch.equal(getattr(wq, fn)(x, repack_layer(wq, Lg)), getattr(wq, fn)(x, repack_layer(wq, LK)))
+    torch.cuda.synchronize()
