@@ -73,13 +73,19 @@ __device__ inline float zero_corr(float z) {
   return z + (DT == F16 ? 1024.0f : 128.0f);
 }
 
-// Waves per workgroup are chosen at launch (1..16); the bound below lets 16.
+// Waves per workgroup are chosen at launch: 1..16, or 1..8 for the variants
+// whose frames need more than the 128 registers a 1024-thread workgroup
+// leaves each lane (four column tiles per wave, 2-bit codes with their
+// 256-row tiles, two column tiles with four groups per unit).
+template <int BITS, int TN, int GPU>
+constexpr bool gemv_big_frames() { return TN >= 4 || BITS == 2 || (TN >= 2 && GPU >= 4); }
+
 // SWIGLU: the layer is a fused gate+up layer repacked with interleaved column
 // tiles (gate, up, gate, up, ...).  Workgroup p owns output tile p: its even
 // waves stream gate tile 2p, its odd waves up tile 2p + 1 (TN = 1, each pair
 // of waves shares one k-range), and the store writes SiLU(gate) * up.
 template <int DT, int BITS, int MODE, int TN, int GPU, bool PACKED, int PF, bool SWIGLU>
-__global__ __launch_bounds__(1024) void gemv_kernel(const GemvArgs a) {
+__global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU>() ? 512 : 1024)) void gemv_kernel(const GemvArgs a) {
   constexpr int KT = BITS == 2 ? 256 : 128;
   constexpr int UPT = KT / 128;                 // 128-row units per tile
   constexpr int WPL = BITS == 3 ? 3 : 4;
@@ -336,12 +342,15 @@ wq_status run(GemvArgs g, int grid, hipStream_t s) {
 // waves over the grid, each streaming an equal share of K; the prefetch depth
 // grows with the tiles a wave streams (deeper prefetch costs registers and
 // out-of-range tail loads, so short ranges keep it at 2).
-inline int pick_waves(int grid, int ktiles, int tn) {
+inline int pick_waves(int grid, int ktiles, bool table, int wmax) {
+  // about 3072 waves in flight (12288 when each workgroup fills an LDS code
+  // table, which caps the workgroups per CU), at most 32 k-tiles per wave,
+  // at least 2
+  const long target = table ? 12288L : 3072L;
   int w = 1;
-  while (w < 16 && (long)grid * w < 3072L && 2 * w <= ktiles && 2 * w * tn <= 16) w *= 2;
+  while (w < wmax && 2 * w <= ktiles && ((long)grid * w < target || ktiles > 32 * w)) w *= 2;
   return w;
 }
-
 template <int DT, int BITS, int MODE, int TN, int GPU, bool PACKED, bool SWIGLU>
 wq_status run_pf(GemvArgs g, int grid, hipStream_t s) {
   const int tpw = g.kt_per_wave;
@@ -362,7 +371,8 @@ wq_status pick_shape(GemvArgs g, hipStream_t s) {
     // size; measured faster than matching its per-wave work with workgroups
     // twice as large.
     const int grid = ntiles / 2;
-    const int kw = max(1, min(pick_waves(ntiles, g.ktiles, 1), 8) / 2);  // waves per column tile
+    const int wmax = gemv_big_frames<BITS, 1, GPU>() ? 8 : 16;
+    const int kw = max(1, pick_waves(ntiles, g.ktiles, MODE == LUT, wmax) / 2);  // waves per column tile
     g.waves = 2 * kw;
     g.kt_per_wave = (g.ktiles + kw - 1) / kw;
     if (g.M <= 4) return run_pf<DT, BITS, MODE, 1, GPU, true, true>(g, grid, s);
@@ -370,16 +380,24 @@ wq_status pick_shape(GemvArgs g, hipStream_t s) {
   }
   if (g.M <= 4) {
     const int grid = ntiles;
-    g.waves = pick_waves(grid, g.ktiles, 1);
+    g.waves = pick_waves(grid, g.ktiles, MODE == LUT, gemv_big_frames<BITS, 1, GPU>() ? 8 : 16);
     g.kt_per_wave = (g.ktiles + g.waves - 1) / g.waves;
     return run_pf<DT, BITS, MODE, 1, GPU, true, false>(g, grid, s);
   }
-  // One activation row per MFMA row; two column tiles per workgroup share the
-  // activation loads when the grid stays large enough.
-  const int tn = (ntiles % 2 == 0 && ntiles / 2 >= 1024) ? 2 : 1;
+  // One activation row per MFMA row.  Each wave loads 16 activation rows per
+  // k-tile -- up to four times the weight bytes of a column tile -- so wide
+  // layers give a wave four (or two) column tiles that share those loads;
+  // narrow layers keep one so that enough workgroups run.
+  int tn = ntiles >= 768 ? 4 : ntiles >= 512 ? 2 : 1;
+  if (BITS == 2 && tn > 2) tn = 2;  // 2-bit frames hold 256 rows: four tiles do not fit the registers
+  while (ntiles % tn != 0) tn /= 2;
   const int grid = ntiles / tn;
-  g.waves = pick_waves(grid, g.ktiles, tn);
+  const bool big = tn == 4 ? gemv_big_frames<BITS, 4, GPU>()
+                 : tn == 2 ? gemv_big_frames<BITS, 2, GPU>() : gemv_big_frames<BITS, 1, GPU>();
+  g.waves = pick_waves(grid, g.ktiles, MODE == LUT, big ? 8 : 16);
   g.kt_per_wave = (g.ktiles + g.waves - 1) / g.waves;
+  if constexpr (BITS != 2)
+    if (tn == 4) return run_pf<DT, BITS, MODE, 4, GPU, false, false>(g, grid, s);
   if (tn == 2) return run_pf<DT, BITS, MODE, 2, GPU, false, false>(g, grid, s);
   return run_pf<DT, BITS, MODE, 1, GPU, false, false>(g, grid, s);
 }
