@@ -15,6 +15,7 @@ replayed, so host-side launch cost does not starve the GPU; the eager
 (launch-by-launch) rate is reported beside it.
 
 Also reported:
+  decode_other_m the same layer set at M = 4 and 16 (graph-replayed);
   roofline      the dominant kernel (the gate+up GEMV, the largest layer)
                 against HBM bandwidth: its launches timed back to back over the
                 rotated copies between HIP events on its stream;
@@ -228,6 +229,33 @@ def main():
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": f"wq_gemv {Ld.name} M={M}", "algorithmic_bytes_per_launch": alg_bytes,
                 "avg_launch_us": round(dom_us, 3), "launches_timed": nd}
+    # the same layer set at the other decode batch sizes of the configuration
+    decode_m = {}
+    for Mx in (4, 16):
+        xm = [to_dev(cfg.x(Mx, L.K), torch.float16) for L in layers]
+        ym = [torch.empty((Mx, L.N), dtype=torch.float16, device=dev) for L in layers]
+        gm = torch.cuda.CUDAGraph()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            for i in range(R):
+                for j in range(len(layers)):
+                    wq.wq_gemv(xm[j], packed[j][i], out=ym[j], stream=cap)
+            with torch.cuda.graph(gm, stream=cap):
+                for i in range(R):
+                    for j in range(len(layers)):
+                        wq.wq_gemv(xm[j], packed[j][i], out=ym[j], stream=cap)
+        stream.wait_stream(cap)
+        torch.cuda.synchronize()
+        gm.replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(replays):
+            gm.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / (replays * R)
+        decode_m[f"M{Mx}"] = {"ms_per_step": round(ms, 5), "weight_GBps": round(set_bytes / (ms * 1e-3) / 1e9, 1)}
+        del gm, xm, ym
     per_kernel = {L.name.split("/")[-1]: {"us_with_events": round(t, 3),
                                           "weight_GBps": round(L.weight_bytes() / (t * 1e-6) / 1e9, 1)}
                   for L, t in zip(layers, kernel_us)}
@@ -528,7 +556,7 @@ def main():
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "eager": {"ms_per_step": round(eager_ms_per_step, 5),
                   "value": round(set_bytes / (eager_ms_per_step * 1e-3) / 1e9, 1)},
-        "roofline": roofline, "per_kernel": per_kernel, "gemm_m2048": gemm,
+        "roofline": roofline, "per_kernel": per_kernel, "decode_other_m": decode_m, "gemm_m2048": gemm,
         "fused_gate_up": fused, "hadamard": had, "fine_zero_groups": fine, "layer_stack": stack, "cpu_baseline": cpu,
         "kernel_sources_sha256_16": khash,
     }

@@ -143,7 +143,7 @@ wq_status wq_dequant_debug(const void* packed, wq_qmode mode, const uint16_t* lu
                            wq_dtype out, void* w, void* stream);
 
 /*
- * wq_gemv -- y [M][N] = x [M][K] . dequant(W), for decode-sized M (1 <= M <= 16;
+ * wq_gemv -- y [M][N] = x [M][K] . dequant(W), for decode-sized M (1 <= M <= 32;
  * WQ_EUNSUPPORTED above).  Matrix-vector products are bound by memory
  * bandwidth and the gain comes from moving fewer weight bytes (exllama
  * bandwidth discussion, GPTQ paper quote and turboderp's reply); this entry

@@ -107,8 +107,8 @@ def test_product_rejects_before_launch(L, fn):
 
 
 def test_gemv_rejects_large_m(L):
-    assert call_product(L, "wq_gemv", M=17) == 2
-    assert call_product(L, "wq_gemv_gate_up", M=17) == 2
+    assert call_product(L, "wq_gemv", M=33) == 2
+    assert call_product(L, "wq_gemv_gate_up", M=33) == 2
 
 
 @pytest.mark.parametrize("fn", ["wq_gemv_gate_up", "wq_gemm_gate_up"])

@@ -62,7 +62,7 @@ def check(orc, wq, fn, L, M, dt, seed):
 @pytest.mark.parametrize("gs", [128, -1])
 def test_fine_gemv_parity(orc, wq, mode, bits, dt, gs):
     K, N = 1024, 96
-    for M in (1, 3, 5, 16):
+    for M in (1, 3, 5, 16, 17, 32):
         print(f"[fine gemv] mode={mode} bits={bits} dt={dt} gs={gs} M={M}", flush=True)
         L = wl.make_layer(K, N, bits, gs, mode, 300 + 7 * mode + bits + dt + M)
         check(orc, wq, "wq_gemv", L, M, dt, 5 + M)

@@ -68,13 +68,13 @@ def check_product(orc, wq, fn, L, M, dt, seed):
 
 GEMV_CASES = [(mode, bits, dt, gs, M, ao)
               for mode in MODES for bits in (2, 3, 4) for dt in (wl.F16, wl.BF16)
-              for gs in (32, 128, -1) for M in (1, 3, 5, 16)
-              for ao in ((False, True) if (gs == 32 and M in (1, 5)) else (False,))]
+              for gs in (32, 128, -1) for M in ((1, 3, 5, 16, 17, 32) if gs == 128 else (1, 3, 5, 16, 32))
+              for ao in ((False, True) if (gs == 32 and M in (1, 5, 32)) else (False,))]
 
 
 @pytest.mark.parametrize("mode,bits,dt,gs,M,ao", GEMV_CASES)
 def test_gemv_parity(orc, wq, mode, bits, dt, gs, M, ao):
-    K, N = 1024, 96  # 4-8 k-tiles, 6 column tiles
+    K, N = 1024, 96  # 4-8 k-tiles, 6 column tiles; M > 16 takes two blocks of 16 rows
     print(f"[gemv] mode={mode} bits={bits} dt={dt} gs={gs} M={M} act_order={ao}", flush=True)
     L = make(mode, bits, gs, K, N, 2000 + 97 * mode + 13 * bits + 5 * dt + M + ao, act_order=ao)
     check_product(orc, wq, "wq_gemv", L, M, dt, 77 + M)
@@ -92,6 +92,29 @@ def test_gemm_parity(orc, wq, mode, bits, dt, gs, M, ao):
     print(f"[gemm] mode={mode} bits={bits} dt={dt} gs={gs} M={M} act_order={ao}", flush=True)
     L = make(mode, bits, gs, K, N, 3000 + 97 * mode + 13 * bits + 5 * dt + M + ao, act_order=ao)
     check_product(orc, wq, "wq_gemm", L, M, dt, 99 + M)
+
+
+@pytest.mark.parametrize("mode", MODES + [wl.ZERO_F16_G16])
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_gemv_wide_two_row_blocks(orc, wq, mode, bits):
+    """A layer wide enough (>= 512 column tiles) for waves that own two column
+    tiles, at M = 32 (two blocks of 16 activation rows; 2-bit codes take a
+    second launch for rows 16..31) and M = 20 (a ragged second block); the
+    oracle computes a seeded sample of columns."""
+    K, N = 512, 8192 + 32
+    L = make(mode, bits, 128 if mode in wl.FINE_ZERO_GROUP else 64, K, N, 4100 + 7 * mode + bits)
+    layer = repack_layer(wq, L)
+    cols = wl.sample_cols(N, 192, seed=bits + mode)
+    cols = np.unique(np.concatenate([cols, np.arange(N - 32, N)])).astype(np.int32)  # the last tiles
+    for M in (32, 20):
+        dt = wl.BF16 if M == 20 else wl.F16
+        print(f"[gemv wide] mode={mode} bits={bits} M={M}", flush=True)
+        x_bits = wl.make_x(M, K, dt, 50 + M)
+        y = wq.wq_gemv(bits_to_tensor(x_bits, act_dtype(dt), "cuda"), layer)
+        torch.cuda.synchronize()
+        got = tensor_f64(y)[:, cols]
+        ok, err, bound = within_tolerance(got, oracle_y(orc, x_bits, dt, L, cols))
+        assert ok, f"max error {err:.3e} > bound {bound:.3e}"
 
 
 def test_m_zero_is_a_noop(wq):

@@ -184,7 +184,7 @@ def _product(fn: str, x: torch.Tensor, layer: PackedLayer, out: Optional[torch.T
 
 
 def wq_gemv(x: torch.Tensor, layer: PackedLayer, out=None, ws=None, stream=None) -> torch.Tensor:
-    """y = x . dequant(W) for 1 <= M <= 16 (decode)."""
+    """y = x . dequant(W) for 1 <= M <= 32 (decode)."""
     return _product("wq_gemv", x, layer, out, ws, stream)
 
 
@@ -194,7 +194,7 @@ def wq_gemm(x: torch.Tensor, layer: PackedLayer, out=None, ws=None, stream=None)
 
 
 def wq_gemv_gate_up(x: torch.Tensor, layer: PackedLayer, out=None, ws=None, stream=None) -> torch.Tensor:
-    """h [M][N/2] = SiLU(x . gate) * (x . up) for 1 <= M <= 16."""
+    """h [M][N/2] = SiLU(x . gate) * (x . up) for 1 <= M <= 32."""
     return _product("wq_gemv_gate_up", x, layer, out, ws, stream)
 
 
@@ -218,10 +218,17 @@ def wq_hadamard(x: torch.Tensor, block: int, out: Optional[torch.Tensor] = None,
     return out
 
 
+# Largest M that linear() sends to wq_gemv (which takes M <= 32).  Measured on
+# MI355X over the LLaMA-7B/70B/405B layer shapes: two blocks of 16 activation
+# rows beat the tiled GEMM up to M = 24 on every shape, and lose to it on the
+# wide and long-K shapes by M = 32.
+GEMV_MAX_M = 24
+
+
 def linear(x: torch.Tensor, layer: PackedLayer, out=None, ws=None, stream=None) -> torch.Tensor:
-    """Decode-sized M goes to wq_gemv, larger M to wq_gemm (the *_gate_up pair for a
-    layer from wq_repack_gate_up)."""
-    small = x.shape[0] <= 16
+    """M <= GEMV_MAX_M goes to wq_gemv, larger M to wq_gemm (the *_gate_up pair for
+    a layer from wq_repack_gate_up)."""
+    small = x.shape[0] <= GEMV_MAX_M
     if layer.gate_up:
         return (wq_gemv_gate_up if small else wq_gemm_gate_up)(x, layer, out, ws, stream)
     return (wq_gemv if small else wq_gemm)(x, layer, out, ws, stream)

@@ -366,7 +366,7 @@ static wq_status product(bool gemm, bool swiglu, const void* x, wq_dtype dt, con
   if (st != WQ_OK) return st;
   if (M < 0) return WQ_EINVAL;
   if (dt != WQ_F16 && dt != WQ_BF16) return WQ_EINVAL;
-  if (!gemm && M > 16) return WQ_EUNSUPPORTED;
+  if (!gemm && M > 32) return WQ_EUNSUPPORTED;
   if (swiglu && N % 32 != 0) return WQ_EUNSUPPORTED;
   if (M == 0) return WQ_OK;
   if (!x || !packed || !y) return WQ_EINVAL;

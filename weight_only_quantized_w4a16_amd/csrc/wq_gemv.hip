@@ -1,4 +1,4 @@
-// wq_gemv.hip -- y = x . dequant(W) for decode-sized M (1..16).
+// wq_gemv.hip -- y = x . dequant(W) for decode-sized M (1..32).
 //
 // Matrix-vector products are bound by memory bandwidth; the quantised kernel
 // wins only by reading fewer weight bytes, while decoding costs extra
@@ -76,16 +76,18 @@ __device__ inline float zero_corr(float z) {
 // Waves per workgroup are chosen at launch: 1..16, or 1..8 for the variants
 // whose frames need more than the 128 registers a 1024-thread workgroup
 // leaves each lane (four column tiles per wave, 2-bit codes with their
-// 256-row tiles, two column tiles with four groups per unit).
-template <int BITS, int TN, int GPU>
-constexpr bool gemv_big_frames() { return TN >= 4 || BITS == 2 || (TN >= 2 && GPU >= 4); }
+// 256-row tiles, two column tiles with four groups per unit, two blocks of
+// 16 activation rows).
+template <int BITS, int TN, int GPU, int MR>
+constexpr bool gemv_big_frames() { return TN >= 4 || BITS == 2 || (TN >= 2 && GPU >= 4) || MR >= 2; }
 
 // SWIGLU: the layer is a fused gate+up layer repacked with interleaved column
 // tiles (gate, up, gate, up, ...).  Workgroup p owns output tile p: its even
 // waves stream gate tile 2p, its odd waves up tile 2p + 1 (TN = 1, each pair
 // of waves shares one k-range), and the store writes SiLU(gate) * up.
-template <int DT, int BITS, int MODE, int TN, int GPU, bool PACKED, int PF, bool SWIGLU>
-__global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU>() ? 512 : 1024)) void gemv_kernel(const GemvArgs a) {
+// MR: blocks of 16 activation rows (standard scheme; M <= 16 MR).
+template <int DT, int BITS, int MODE, int TN, int GPU, bool PACKED, int PF, bool SWIGLU, int MR>
+__global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU, MR>() ? 512 : 1024)) void gemv_kernel(const GemvArgs a) {
   constexpr int KT = BITS == 2 ? 256 : 128;
   constexpr int UPT = KT / 128;                 // 128-row units per tile
   constexpr int WPL = BITS == 3 ? 3 : 4;
@@ -104,7 +106,8 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU>() ? 512 : 1024)) vo
   constexpr int NRED = PACKED ? 1 : 4;          // reduced values per lane per column tile
 
   __shared__ uint32_t table[TABLE ? (32 << (2 * BITS)) : 1];
-  extern __shared__ float red[];                // [waves][TN][NRED][64]
+  extern __shared__ float red[];                // [waves][TN][MR][NRED][64]
+  static_assert(!PACKED || MR == 1, "the packed scheme holds at most 4 rows");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar arithmetic
@@ -120,9 +123,13 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU>() ? 512 : 1024)) vo
   // Buffer offsets = per-lane vector part + per-tile scalar part.  The vector
   // part becomes kOutOfRange for loads that must return zero (rows past M,
   // tiles past the wave's range).
-  //   packed:   lane c -> (m = c / 4, k-block c % 4) ; standard: lane c -> m = c
-  const int xm = PACKED ? (c >> 2) : c;
-  const uint32_t x_lane = xm < a.M ? (uint32_t)(xm * a.K + 8 * h + (PACKED ? 32 * (c & 3) : 0)) * 2u : kOutOfRange;
+  //   packed:   lane c -> (m = c / 4, k-block c % 4) ; standard: lane c -> m = 16 r + c
+  uint32_t x_lane[MR];
+#pragma unroll
+  for (int r = 0; r < MR; ++r) {
+    const int xm = PACKED ? (c >> 2) : 16 * r + c;
+    x_lane[r] = xm < a.M ? (uint32_t)(xm * a.K + 8 * h + (PACKED ? 32 * (c & 3) : 0)) * 2u : kOutOfRange;
+  }
   const uint32_t w_lane = (uint32_t)lane * WPL * 4;
   const uint32_t s_lane = (uint32_t)c * REC;
   const uint32_t zp_lane = (uint32_t)(c >> 3) * ZREC;
@@ -137,7 +144,7 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU>() ? 512 : 1024)) vo
 
   struct Frame {
     uint32_t w[TN][WPL];
-    u32x4 xa[NXA];
+    u32x4 xa[MR][NXA];
     uint32_t s[TN][UPT][SW];                  // scale record (with fp16 zero-points when Z16)
     uint32_t z[TN][UPT][ZW];                  // packed or fine zero-point record
   };
@@ -159,12 +166,15 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU>() ? 512 : 1024)) vo
         f.w[t][0] = v[0]; f.w[t][1] = v[1]; f.w[t][2] = v[2];
       }
     }
-    const uint32_t xv = ok ? x_lane : kOutOfRange;
 #pragma unroll
-    for (int i = 0; i < NXA; ++i) {
-      // packed: unit i covers rows 128 i ..; standard: k-block i covers rows 32 i ..
-      const uint32_t koff = (uint32_t)(ktc * KT + (PACKED ? 128 * i : 32 * i)) * 2u;
-      f.xa[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, xv, koff, 0);
+    for (int r = 0; r < MR; ++r) {
+      const uint32_t xv = ok ? x_lane[r] : kOutOfRange;
+#pragma unroll
+      for (int i = 0; i < NXA; ++i) {
+        // packed: unit i covers rows 128 i ..; standard: k-block i covers rows 32 i ..
+        const uint32_t koff = (uint32_t)(ktc * KT + (PACKED ? 128 * i : 32 * i)) * 2u;
+        f.xa[r][i] = __builtin_amdgcn_raw_buffer_load_b128(rx, xv, koff, 0);
+      }
     }
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
@@ -193,11 +203,13 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU>() ? 512 : 1024)) vo
   const uint32_t* tab = table + (lane & 31);
   const DecodeConsts dk = make_decode_consts<DT>();
 
-  float tot[TN][4];
+  float tot[MR][TN][4];
 #pragma unroll
-  for (int t = 0; t < TN; ++t)
+  for (int r = 0; r < MR; ++r)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) tot[t][e] = 0.0f;
+    for (int t = 0; t < TN; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tot[r][t][e] = 0.0f;
 
   // zero-point of group j of unit u of column tile t
   auto zero_of = [&](const Frame& f, int t, int u, int j) -> float {
@@ -220,11 +232,11 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU>() ? 512 : 1024)) vo
             const u32x4 b = decode_frag<BITS, DT, MODE, 4 * u + kb>(
                 f.w[t], tab, dk, FINE ? fine_zero_bits(f.z[t][u], kb) : 0u,
                 SCALED ? rec_scale<Z16>(f.s[t][u], kb / KBPG) : 0.0f);
-            acc[t][kb] = mfma16<DT>(f.xa[u], b, zero4);
+            acc[t][kb] = mfma16<DT>(f.xa[0][u], b, zero4);
           }
         });
         f4 xs = zero4;
-        if constexpr (XS) xs = mfma16<DT>(f.xa[u], ones_frag<DT>(), zero4);
+        if constexpr (XS) xs = mfma16<DT>(f.xa[0][u], ones_frag<DT>(), zero4);
         // element e of this lane = row 4m + e = k-block e of the unit
 #pragma unroll
         for (int t = 0; t < TN; ++t) {
@@ -234,16 +246,20 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU>() ? 512 : 1024)) vo
             const float s = SCALED ? 1.0f : rec_scale<Z16>(f.s[t][u], j);
             float v = acc[t][e][e];
             if constexpr (XS) v = __builtin_fmaf(-zero_corr<DT>(zero_of(f, t, u, j)), xs[e], v);
-            tot[t][e] = __builtin_fmaf(s, v, tot[t][e]);
+            tot[0][t][e] = __builtin_fmaf(s, v, tot[0][t][e]);
           }
         }
       } else {
         sfor<GPU>([&](auto gc) {
           constexpr int gi = decltype(gc)::value;
-          f4 acc[TN];
+          f4 acc[MR][TN];
+          f4 xs[MR];
 #pragma unroll
-          for (int t = 0; t < TN; ++t) acc[t] = zero4;
-          f4 xs = zero4;
+          for (int r = 0; r < MR; ++r) {
+            xs[r] = zero4;
+#pragma unroll
+            for (int t = 0; t < TN; ++t) acc[r][t] = zero4;
+          }
           sfor<KBPG>([&](auto kc) {
             constexpr int kb = 4 * u + gi * KBPG + decltype(kc)::value;  // k-block inside the tile
 #pragma unroll
@@ -251,20 +267,25 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU>() ? 512 : 1024)) vo
               const u32x4 b = decode_frag<BITS, DT, MODE, kb>(
                   f.w[t], tab, dk, FINE ? fine_zero_bits(f.z[t][u], kb - 4 * u) : 0u,
                   SCALED ? rec_scale<Z16>(f.s[t][u], gi) : 0.0f);
-              acc[t] = mfma16<DT>(f.xa[kb], b, acc[t]);
+#pragma unroll
+              for (int r = 0; r < MR; ++r) acc[r][t] = mfma16<DT>(f.xa[r][kb], b, acc[r][t]);
             }
-            if constexpr (XS) xs = mfma16<DT>(f.xa[kb], ones_frag<DT>(), xs);
+            if constexpr (XS)
+#pragma unroll
+              for (int r = 0; r < MR; ++r) xs[r] = mfma16<DT>(f.xa[r][kb], ones_frag<DT>(), xs[r]);
           });
 #pragma unroll
           for (int t = 0; t < TN; ++t) {
             const float s = SCALED ? 1.0f : rec_scale<Z16>(f.s[t][u], gi);
             const float cz = XS ? zero_corr<DT>(zero_of(f, t, u, gi)) : 0.0f;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              float v = acc[t][e];
-              if constexpr (XS) v = __builtin_fmaf(-cz, xs[e], v);
-              tot[t][e] = __builtin_fmaf(s, v, tot[t][e]);
-            }
+            for (int r = 0; r < MR; ++r)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                float v = acc[r][t][e];
+                if constexpr (XS) v = __builtin_fmaf(-cz, xs[r][e], v);
+                tot[r][t][e] = __builtin_fmaf(s, v, tot[r][t][e]);
+              }
           }
         });
       }
@@ -292,24 +313,26 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU>() ? 512 : 1024)) vo
 
   // Cross-wave reduction and store.
 #pragma unroll
-  for (int t = 0; t < TN; ++t) {
-    float* r = red + ((size_t)(wave * TN + t) * NRED) * 64;
-    if constexpr (PACKED) {
-      r[lane] = (tot[t][0] + tot[t][1]) + (tot[t][2] + tot[t][3]);
-    } else {
+  for (int t = 0; t < TN; ++t)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) r[e * 64 + lane] = tot[t][e];
+    for (int r = 0; r < MR; ++r) {
+      float* dst = red + ((size_t)((wave * TN + t) * MR + r) * NRED) * 64;
+      if constexpr (PACKED) {
+        dst[lane] = (tot[r][t][0] + tot[r][t][1]) + (tot[r][t][2] + tot[r][t][3]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[e * 64 + lane] = tot[r][t][e];
+      }
     }
-  }
   __syncthreads();
   static_assert(!SWIGLU || TN == 1, "gate and up tiles sit on different waves");
-  constexpr int SLOTS = TN * NRED * 64;
+  constexpr int SLOTS = TN * MR * NRED * 64;
   for (int i = threadIdx.x; i < SLOTS; i += a.waves * 64) {
-    const int l = i & 63, e = (i >> 6) % NRED, t = i / (64 * NRED);
+    const int l = i & 63, e = (i >> 6) % NRED, rb = (i / (64 * NRED)) % MR, t = i / (64 * NRED * MR);
     // sum over the waves w0, w0 + step, ... of tile t's partial results
     auto reduce = [&](int w0, int step) {
       float v = 0.0f;
-      for (int w = w0; w < a.waves; w += step) v += red[((size_t)(w * TN + t) * NRED + e) * 64 + l];
+      for (int w = w0; w < a.waves; w += step) v += red[((size_t)((w * TN + t) * MR + rb) * NRED + e) * 64 + l];
       return v;
     };
     float v;
@@ -319,8 +342,8 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU>() ? 512 : 1024)) vo
     } else {
       v = reduce(0, 1);
     }
-    // packed: lane l = 16 m + col ; standard: row 4 (l / 16) + e, col l % 16
-    const int m = PACKED ? (l >> 4) : 4 * (l >> 4) + e;
+    // packed: lane l = 16 m + col ; standard: row 16 rb + 4 (l / 16) + e, col l % 16
+    const int m = PACKED ? (l >> 4) : 16 * rb + 4 * (l >> 4) + e;
     const int n = (SWIGLU ? (int)blockIdx.x : nt0 + t) * 16 + (l & 15);
     if (m < a.M) a.y[(size_t)m * a.ldy + n] = DT == F16 ? f32_to_f16(v) : f32_to_bf16(v);
   }
@@ -329,12 +352,12 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU>() ? 512 : 1024)) vo
 // ---------------------------------------------------------------------------
 // Launch-shape choice and dispatch.
 // ---------------------------------------------------------------------------
-template <int DT, int BITS, int MODE, int TN, int GPU, bool PACKED, int PF, bool SWIGLU>
+template <int DT, int BITS, int MODE, int TN, int GPU, bool PACKED, int PF, bool SWIGLU, int MR>
 wq_status run(GemvArgs g, int grid, hipStream_t s) {
   constexpr int NRED = PACKED ? 1 : 4;
-  const size_t lds = (size_t)g.waves * TN * NRED * 64 * sizeof(float);
-  hipLaunchKernelGGL((gemv_kernel<DT, BITS, MODE, TN, GPU, PACKED, PF, SWIGLU>), dim3(grid), dim3(g.waves * 64), lds,
-                     s, g);
+  const size_t lds = (size_t)g.waves * TN * MR * NRED * 64 * sizeof(float);
+  hipLaunchKernelGGL((gemv_kernel<DT, BITS, MODE, TN, GPU, PACKED, PF, SWIGLU, MR>), dim3(grid), dim3(g.waves * 64),
+                     lds, s, g);
   return launch_status();
 }
 
@@ -351,55 +374,84 @@ inline int pick_waves(int grid, int ktiles, bool table, int wmax) {
   while (w < wmax && 2 * w <= ktiles && ((long)grid * w < target || ktiles > 32 * w)) w *= 2;
   return w;
 }
-template <int DT, int BITS, int MODE, int TN, int GPU, bool PACKED, bool SWIGLU>
+template <int DT, int BITS, int MODE, int TN, int GPU, bool PACKED, bool SWIGLU, int MR>
 wq_status run_pf(GemvArgs g, int grid, hipStream_t s) {
   const int tpw = g.kt_per_wave;
   if constexpr (PACKED) {
-    if (tpw >= 8) return run<DT, BITS, MODE, TN, GPU, PACKED, 4, SWIGLU>(g, grid, s);
-    if (tpw >= 5) return run<DT, BITS, MODE, TN, GPU, PACKED, 3, SWIGLU>(g, grid, s);
+    if (tpw >= 8) return run<DT, BITS, MODE, TN, GPU, PACKED, 4, SWIGLU, MR>(g, grid, s);
+    if (tpw >= 5) return run<DT, BITS, MODE, TN, GPU, PACKED, 3, SWIGLU, MR>(g, grid, s);
   }
-  return run<DT, BITS, MODE, TN, GPU, PACKED, 2, SWIGLU>(g, grid, s);
+  return run<DT, BITS, MODE, TN, GPU, PACKED, 2, SWIGLU, MR>(g, grid, s);
 }
 
-template <int DT, int BITS, int MODE, int GPU, bool SWIGLU>
-wq_status pick_shape(GemvArgs g, hipStream_t s) {
+// Standard scheme (one activation row per MFMA row, MR blocks of 16 rows).
+template <int DT, int BITS, int MODE, int GPU, bool SWIGLU, int MR>
+wq_status pick_standard(GemvArgs g, hipStream_t s) {
   const int ntiles = g.N / 16;
-  if (SWIGLU) {
+  if constexpr (SWIGLU) {
     // One workgroup per output tile, its waves split between the gate and up
     // tiles.  Half the waves per column tile of the plain product (each
     // streaming twice the k-range) keeps the workgroup at the plain product's
     // size; measured faster than matching its per-wave work with workgroups
     // twice as large.
-    const int grid = ntiles / 2;
-    const int wmax = gemv_big_frames<BITS, 1, GPU>() ? 8 : 16;
+    const int wmax = gemv_big_frames<BITS, 1, GPU, MR>() ? 8 : 16;
     const int kw = max(1, pick_waves(ntiles, g.ktiles, MODE == LUT, wmax) / 2);  // waves per column tile
     g.waves = 2 * kw;
     g.kt_per_wave = (g.ktiles + kw - 1) / kw;
-    if (g.M <= 4) return run_pf<DT, BITS, MODE, 1, GPU, true, true>(g, grid, s);
-    return run_pf<DT, BITS, MODE, 1, GPU, false, true>(g, grid, s);
-  }
-  if (g.M <= 4) {
-    const int grid = ntiles;
-    g.waves = pick_waves(grid, g.ktiles, MODE == LUT, gemv_big_frames<BITS, 1, GPU>() ? 8 : 16);
+    return run_pf<DT, BITS, MODE, 1, GPU, false, true, MR>(g, ntiles / 2, s);
+  } else {
+    // Each wave loads 16 activation rows per row block and k-tile -- up to four
+    // times the weight bytes of a column tile -- so wide layers give a wave
+    // four (or two) column tiles that share those loads; narrow layers keep one
+    // so that enough workgroups run.
+    int tn = ntiles >= 768 ? 4 : ntiles >= 512 ? 2 : 1;
+    // 2-bit frames hold 256 rows, and a second row block doubles the activation
+    // frames: four tiles would not fit the registers
+    if ((BITS == 2 || MR == 2) && tn > 2) tn = 2;
+    while (ntiles % tn != 0) tn /= 2;
+    const int grid = ntiles / tn;
+    const bool big = tn == 4 ? gemv_big_frames<BITS, 4, GPU, MR>()
+                   : tn == 2 ? gemv_big_frames<BITS, 2, GPU, MR>() : gemv_big_frames<BITS, 1, GPU, MR>();
+    g.waves = pick_waves(grid, g.ktiles, MODE == LUT, big ? 8 : 16);
     g.kt_per_wave = (g.ktiles + g.waves - 1) / g.waves;
-    return run_pf<DT, BITS, MODE, 1, GPU, true, false>(g, grid, s);
+    if constexpr (BITS != 2 && MR == 1)
+      if (tn == 4) return run_pf<DT, BITS, MODE, 4, GPU, false, false, MR>(g, grid, s);
+    if (tn == 2) return run_pf<DT, BITS, MODE, 2, GPU, false, false, MR>(g, grid, s);
+    return run_pf<DT, BITS, MODE, 1, GPU, false, false, MR>(g, grid, s);
   }
-  // One activation row per MFMA row.  Each wave loads 16 activation rows per
-  // k-tile -- up to four times the weight bytes of a column tile -- so wide
-  // layers give a wave four (or two) column tiles that share those loads;
-  // narrow layers keep one so that enough workgroups run.
-  int tn = ntiles >= 768 ? 4 : ntiles >= 512 ? 2 : 1;
-  if (BITS == 2 && tn > 2) tn = 2;  // 2-bit frames hold 256 rows: four tiles do not fit the registers
-  while (ntiles % tn != 0) tn /= 2;
-  const int grid = ntiles / tn;
-  const bool big = tn == 4 ? gemv_big_frames<BITS, 4, GPU>()
-                 : tn == 2 ? gemv_big_frames<BITS, 2, GPU>() : gemv_big_frames<BITS, 1, GPU>();
-  g.waves = pick_waves(grid, g.ktiles, MODE == LUT, big ? 8 : 16);
-  g.kt_per_wave = (g.ktiles + g.waves - 1) / g.waves;
-  if constexpr (BITS != 2)
-    if (tn == 4) return run_pf<DT, BITS, MODE, 4, GPU, false, false>(g, grid, s);
-  if (tn == 2) return run_pf<DT, BITS, MODE, 2, GPU, false, false>(g, grid, s);
-  return run_pf<DT, BITS, MODE, 1, GPU, false, false>(g, grid, s);
+}
+
+template <int DT, int BITS, int MODE, int GPU, bool SWIGLU>
+wq_status pick_shape(GemvArgs g, hipStream_t s) {
+  const int ntiles = g.N / 16;
+  if (g.M > 16) {
+    if constexpr (BITS == 2) {
+      // Two row blocks of 2-bit frames (256 rows) do not fit the registers:
+      // rows 16.. go through a second launch (the weights are streamed twice).
+      GemvArgs hi = g;
+      hi.x += (size_t)16 * g.K;
+      hi.y += (size_t)16 * g.ldy;
+      hi.M = g.M - 16;
+      g.M = 16;
+      const wq_status st = pick_standard<DT, BITS, MODE, GPU, SWIGLU, 1>(g, s);
+      return st != WQ_OK ? st : pick_standard<DT, BITS, MODE, GPU, SWIGLU, 1>(hi, s);
+    } else {
+      return pick_standard<DT, BITS, MODE, GPU, SWIGLU, 2>(g, s);
+    }
+  }
+  if (g.M > 4) return pick_standard<DT, BITS, MODE, GPU, SWIGLU, 1>(g, s);
+  // Packed scheme: M <= 4 rows x 4 k-blocks in the 16 MFMA rows.
+  const int wmax = gemv_big_frames<BITS, 1, GPU, 1>() ? 8 : 16;
+  if constexpr (SWIGLU) {
+    const int kw = max(1, pick_waves(ntiles, g.ktiles, MODE == LUT, wmax) / 2);  // waves per column tile
+    g.waves = 2 * kw;
+    g.kt_per_wave = (g.ktiles + kw - 1) / kw;
+    return run_pf<DT, BITS, MODE, 1, GPU, true, true, 1>(g, ntiles / 2, s);
+  } else {
+    g.waves = pick_waves(ntiles, g.ktiles, MODE == LUT, wmax);
+    g.kt_per_wave = (g.ktiles + g.waves - 1) / g.waves;
+    return run_pf<DT, BITS, MODE, 1, GPU, true, false, 1>(g, ntiles, s);
+  }
 }
 
 }  // namespace
