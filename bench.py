@@ -66,6 +66,11 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--copy-probe", action="store_true",
                    help="also run a plain device copy of known size (counter calibration)")
+    p.add_argument("--points", action="store_true",
+                   help="instead of the step: time every configuration point (all shapes, M, bits and "
+                        "groups of the workloads) against its roofline, plus context numbers")
+    p.add_argument("--points-configs", default="1,2,3,4,5,6",
+                   help="configurations for --points (comma-separated ids)")
     return p.parse_args()
 
 
@@ -96,12 +101,164 @@ def read_traffic(khash):
         return None
 
 
+def run_points(args):
+    """Every configuration point (layer shape x M x code width x group) through
+    the product entry point a caller uses (linear(): the GEMV for decode-sized M,
+    the GEMM above), timed as back-to-back launches over R rotated copies of the
+    layer (R x weight bytes > 1 GiB) captured in a HIP graph and replayed; the
+    median of 5 replays.  Each point is set against t_ideal = max(algorithmic
+    bytes / 8 TB/s, 2MNK / 2.5 PFLOP/s).  Context: single-call latency with a
+    cold last-level cache (512 MB written in between), torch's own streaming
+    read and copy over 2 GiB, and torch.matmul in fp16 on weights dequantised
+    at load time (wq_dequant_debug) at the prefill shapes."""
+    import statistics
+
+    import numpy as np
+    import torch
+
+    import weight_only_quantized_w4a16_amd as wq
+    import workloads as wl
+
+    wq.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    s = torch.cuda.Stream()
+
+    def to_dev(a, dtype):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(dtype).to(dev)
+        return torch.from_numpy(a.view(np.int32)).to(dev)
+
+    def repack(L):
+        q = to_dev(L.qweight, torch.int32)
+        sc = to_dev(L.scales, torch.float16)
+        z = None
+        if L.mode == wl.ZERO_F16 or L.mode in wl.FINE_ZERO_GROUP:
+            z = to_dev(L.zeros, torch.float16)
+        elif L.mode == wl.ZERO_PACKED:
+            z = to_dev(L.zeros, torch.int32)
+        lut = to_dev(L.lut, torch.float16) if L.lut is not None else None
+        return wq.wq_repack(q, sc, z, L.mode, L.g_idx, L.K, L.N, L.bits, L.group_size, lut=lut)
+
+    def graph_time(fn, n):
+        """fn(i) launches call i on stream s; n calls per replay; median us per call."""
+        with torch.cuda.stream(s):
+            for i in range(n):
+                fn(i)
+        s.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for i in range(n):
+                    fn(i)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            g.replay()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(5):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(s):  # replay() launches on the current stream
+                e0.record(s)
+                g.replay()
+                e1.record(s)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) / n * 1e3)
+        del g
+        return statistics.median(ts)
+
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    points, cold = [], []
+    want = {int(c) for c in args.points_configs.split(",")}
+    for cid, cfg in wl.CONFIGS.items():
+        if cid not in want:
+            continue
+        tdt = torch.float16 if cfg.dtype == wl.F16 else torch.bfloat16
+        for (lname, K, N) in cfg.layers:
+            for bits in cfg.bits:
+                for gs in cfg.groups:
+                    L = cfg.layer(lname, bits, gs)
+                    wb = L.weight_bytes()
+                    R = max(2, -(-(1 << 30) // wb))
+                    copies = [repack(L) for _ in range(R)]
+                    for M in cfg.Ms:
+                        x = to_dev(cfg.x(M, K), tdt)
+                        y = torch.empty((M, N), dtype=tdt, device=dev)
+                        has_perm = copies[0].perm is not None
+                        ws = torch.empty(max(wq.wq_workspace_bytes(M, N, K, bits, has_perm), 16),
+                                         dtype=torch.uint8, device=dev)
+                        path = "gemv" if M <= wq.GEMV_MAX_M else "gemm"
+                        n = R * max(1, -(-8 // R))
+                        us = graph_time(lambda i: wq.linear(x, copies[i % R], out=y, ws=ws, stream=s), n)
+                        flops = 2.0 * M * N * K
+                        alg = wb + 2 * M * K + 2 * M * N + (4 * K if has_perm else 0)
+                        t_ideal = max(alg / (HBM_PEAK_GBS * 1e3), flops / (MFMA_F16_PEAK_TFLOPS * 1e6))
+                        points.append({"config": cfg.name, "layer": f"{lname} {K}x{N}", "bits": bits,
+                                       "group": gs, "M": M, "path": path, "us": round(us, 2),
+                                       "weight_GBps": round(wb / us / 1e3, 1),
+                                       "tflops": round(flops / us / 1e6, 1),
+                                       "t_ideal_us": round(t_ideal, 2), "frac_of_ideal": round(t_ideal / us, 3)})
+                        print(f"[points] {points[-1]}", file=sys.stderr, flush=True)
+                        if M == 1 and cid in (1, 2):
+                            # one call after 512 MB of writes (the last-level cache holds none of it)
+                            ts = []
+                            for r in range(5):
+                                with torch.cuda.stream(s):
+                                    scratch.fill_(r)
+                                e0 = torch.cuda.Event(enable_timing=True)
+                                e1 = torch.cuda.Event(enable_timing=True)
+                                e0.record(s)
+                                wq.linear(x, copies[r % R], out=y, ws=ws, stream=s)
+                                e1.record(s)
+                                torch.cuda.synchronize()
+                                ts.append(e0.elapsed_time(e1) * 1e3)
+                            cold.append({"config": cfg.name, "layer": f"{lname} {K}x{N}", "M": 1,
+                                         "us": round(statistics.median(ts), 2)})
+                        del x, y, ws
+                    del copies
+                    torch.cuda.empty_cache()
+    del scratch
+    # torch's own streaming kernels over 2 GiB (context for what a read can reach)
+    big = torch.empty(1 << 31, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(big)
+    v = big.view(torch.int32)
+    read_us = graph_time(lambda i: v.sum(dtype=torch.int64), 4)
+    copy_us = graph_time(lambda i: dst.copy_(big), 4)
+    del big, dst, v
+    torch.cuda.empty_cache()
+    stream_ctx = {"bytes": 1 << 31, "torch_sum_read_GBps": round((1 << 31) / read_us / 1e3, 1),
+                  "torch_copy_read_plus_write_GBps": round(2 * (1 << 31) / copy_us / 1e3, 1)}
+    # dense fp16 comparator: torch.matmul on weights dequantised at load time
+    dense = []
+    if 3 in want:
+        c3 = wl.CONFIGS[3]
+        for (lname, K, N) in c3.layers:
+            layer = repack(c3.layer(lname, 4, -1))
+            W = wq.wq_dequant_debug(layer, torch.float16)
+            del layer
+            for M in c3.Ms:
+                x = to_dev(c3.x(M, K), torch.float16)
+                y = torch.empty((M, N), dtype=torch.float16, device=dev)
+                us = graph_time(lambda i: torch.matmul(x, W, out=y), 4)
+                dense.append({"layer": f"{lname} {K}x{N}", "M": M, "us": round(us, 2),
+                              "tflops": round(2.0 * M * N * K / us / 1e6, 1)})
+            del W
+            torch.cuda.empty_cache()
+    print(json.dumps({"points": points, "cold_single_call": cold, "stream_2GiB": stream_ctx,
+                      "dense_fp16_torch_matmul": dense}))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: every box here has one, and this product path is "
               f"single-GPU (asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
+    if args.points:
+        run_points(args)
+        return
 
     import numpy as np
     import torch

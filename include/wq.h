@@ -102,9 +102,10 @@ size_t wq_packed_bytes(int K, int N, int bits, int group_size, wq_qmode mode);
  * Scratch memory wq_gemv / wq_gemm (and their *_gate_up forms) need for a call
  * with these sizes: the permuted copy of x when act-order is used (M*K
  * activation elements, 2 bytes each, rounded up to 256 bytes), then, for
- * wq_gemm on narrow problems (M <= 64 and too few 256-column workgroups to
- * fill the GPU), the fp32 partial products of a K split (S*M*N*4 bytes, S the
- * number of K slices, a function of M, N, K and bits).  0 when neither applies.
+ * wq_gemm on problems too small to fill the GPU (fewer than 256 workgroups of
+ * 64 rows x 256 columns), the fp32 partial products of a K split (S*M*N*4
+ * bytes, S the number of K slices, a function of M, N, K and bits).  0 when
+ * neither applies.
  */
 size_t wq_workspace_bytes(int M, int N, int K, int bits, int has_perm);
 

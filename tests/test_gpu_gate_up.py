@@ -142,7 +142,7 @@ def test_gemm_gate_up_k_split(orc, wq, mode, dt):
     applies SiLU(gate) * up to the summed halves."""
     K, N = 2048, 448
     for gs in (128, -1):
-        for M in (1, 33):
+        for M in (1, 33, 130):
             L = make(mode, 4, gs, K, N, 7500 + mode + dt + M)
             check_gate_up(orc, wq, "wq_gemm_gate_up", L, M, dt, 77 + M)
 

@@ -192,12 +192,13 @@ KSPLIT_CASES = [(mode, bits, dt, gs) for mode in MODES for bits in (2, 4) for dt
 
 @pytest.mark.parametrize("mode,bits,dt,gs", KSPLIT_CASES)
 def test_gemm_k_split_parity(orc, wq, mode, bits, dt, gs):
-    """Narrow large-M products split K over several workgroups (fp32 partial
-    sums in the workspace, summed by a second kernel): 224 columns and
-    K = 2048 give 4 slices, for M = 1, 17, 64 and the last slice ragged."""
+    """Narrow products split K over several workgroups (fp32 partial sums in
+    the workspace, summed by a second kernel): 224 columns and K = 2048 give 4
+    slices, for M = 1, 17, 64, 130 and 300 (ragged row and column tiles)."""
     K, N = 2048, 224
     assert wq.wq_workspace_bytes(64, N, K, bits, False) > 0
-    for M in (1, 17, 64):
+    assert wq.wq_workspace_bytes(300, N, K, bits, False) > 0
+    for M in (1, 17, 64, 130, 300):
         print(f"[gemm k-split] mode={mode} bits={bits} dt={dt} gs={gs} M={M}", flush=True)
         L = make(mode, bits, gs, K, N, 8000 + 97 * mode + 13 * bits + 5 * dt + M)
         check_product(orc, wq, "wq_gemm", L, M, dt, 123 + M)

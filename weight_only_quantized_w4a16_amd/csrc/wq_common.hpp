@@ -38,15 +38,16 @@ inline wq_status check_layer(int K, int N, int bits, int group_size, int mode) {
   return WQ_OK;
 }
 
-// K split of the large-M product.  Workgroups cover 256 columns and (for
-// M <= 64) all rows, so a narrow layer leaves most of the GPU idle; its K range
-// is then split until about 512 workgroups run, keeping at least 4 k-tiles per
-// split.  The partial products go through an fp32 workspace.
+// K split of the large-M product.  A workgroup covers 256 columns and 64 rows
+// when the grid is small, so a narrow layer at moderate M (fewer such
+// workgroups than CUs) leaves most of the GPU idle; its K range is then split
+// until about 512 workgroups run, keeping at least 4 k-tiles per split.  The
+// partial products go through an fp32 workspace.
 inline int gemm_ksplit(int M, int N, int K, int bits) {
-  if (M > 64) return 1;
-  const int nwg = (N + 255) / 256;
+  const long nwg = (long)((M + 63) / 64) * ((N + 255) / 256);  // 64 x 256 workgroups
+  if (nwg >= 256) return 1;
   const int ktiles = K / tile_k(bits);
-  int s = (512 + nwg - 1) / nwg;
+  int s = (int)((512 + nwg - 1) / nwg);
   if (s > ktiles / 4) s = ktiles / 4;
   if (s <= 1) return 1;
   const int per = (ktiles + s - 1) / s;  // k-tiles per split; no split left empty

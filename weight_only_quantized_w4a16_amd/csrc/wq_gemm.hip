@@ -430,13 +430,15 @@ __global__ __launch_bounds__(256) void ksplit_reduce_kernel(const float* __restr
 
 template <int DT, int BITS, int MODE, int GPU, bool EPI>
 wq_status run_gemm(GemmArgs g, hipStream_t s) {
-  // 128-row tiles unless that leaves fewer than about two workgroups per CU.
-  // Modes whose decode needs more registers (fp16 zero-points, tables) run
-  // 64-row tiles: at 128 rows they spill (or drop to one wave per SIMD), which
-  // measured slower than decoding each weight for half as many rows.
+  // 128-row tiles unless that leaves fewer than about two workgroups per CU
+  // (a K split always runs 64-row tiles).  Modes whose decode needs more
+  // registers (fp16 zero-points, tables) run 64-row tiles: at 128 rows they
+  // spill (or drop to one wave per SIMD), which measured slower than decoding
+  // each weight for half as many rows.
   constexpr bool HEAVY = MODE == ZERO_F16 || MODE == LUT || MODE == ZFINE;
   g.ntiles_wg = (g.N + 255) / 256;
-  const int bm = (HEAVY || g.M <= 64 || (long)((g.M + 127) / 128) * g.ntiles_wg < 480) ? 64 : 128;
+  const int bm =
+      (HEAVY || g.ksplit > 1 || g.M <= 64 || (long)((g.M + 127) / 128) * g.ntiles_wg < 480) ? 64 : 128;
   g.mtiles = (g.M + bm - 1) / bm;
   g.ktps = (g.ktiles + g.ksplit - 1) / g.ksplit;
   const int grid = g.mtiles * g.ntiles_wg * g.ksplit;
