@@ -31,6 +31,8 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 
 // Raw buffer resources: a load whose offset lies past num_records returns zero
 // without touching memory, which lets prefetches past the end of a range stay
@@ -59,14 +61,14 @@ __device__ inline float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32
 __device__ inline uint16_t f32_to_f16(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
 __device__ inline uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
-// Round a pair of fp32 values (each exactly representable in fp32) to the
-// activation dtype with round-to-nearest-even; lo in bits 0..15.
+// Round a pair of fp32 values to the activation dtype with
+// round-to-nearest-even; lo in bits 0..15 (one v_cvt_pk_{f16,bf16}_f32).
 template <int DT>
 __device__ inline uint32_t pack2(float lo, float hi) {
   if constexpr (DT == F16) {
-    return (uint32_t)f32_to_f16(lo) | ((uint32_t)f32_to_f16(hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){lo, hi}, h2));
   } else {
-    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){lo, hi}, bf2));
   }
 }
 
@@ -97,6 +99,8 @@ struct DecodeConsts {
   uint32_t m4lo, m4hi;  // 0x000F000F, 0x00F000F0
   uint32_t m2[5];       // 0x00030003 << 2i
   uint32_t magic;       // kMagicF16 or kMagicBF16
+  uint32_t magic_h;     // kMagicF16 (exact bf16 decode: fp16 halves widened by v_fma_mix)
+  float nzero;          // -0.0f, an addend the compiler cannot fold away
 };
 
 template <int DT>
@@ -107,11 +111,17 @@ __device__ inline DecodeConsts make_decode_consts() {
 #pragma unroll
   for (int i = 0; i < 5; ++i) k.m2[i] = 0x00030003u << (2 * i);
   k.magic = DT == F16 ? kMagicF16 : kMagicBF16;
+  k.magic_h = kMagicF16;
+  k.nzero = -0.0f;
   asm volatile("" : "+s"(k.m4lo));
   asm volatile("" : "+s"(k.m4hi));
 #pragma unroll
   for (int i = 0; i < 5; ++i) asm volatile("" : "+s"(k.m2[i]));
   asm volatile("" : "+v"(k.magic));
+  if constexpr (DT == BF16) {
+    asm volatile("" : "+v"(k.magic_h));
+    asm volatile("" : "+v"(k.nzero));
+  }
   return k;
 }
 
@@ -194,19 +204,20 @@ __device__ inline u32x4 offset_frag(const uint32_t* w, const DecodeConsts& k) {
 // (bias 1024 for fp16, 128 for bf16), one shift and one AND-OR per register
 // and no float arithmetic; the caller removes bias + z with the row sums of x.
 // ---------------------------------------------------------------------------
+// `magic` is k.magic (the activation dtype's bias) unless given.
 template <int BITS, int KB>
-__device__ inline u32x4 biased_frag(const uint32_t* w, const DecodeConsts& k) {
+__device__ inline u32x4 biased_frag(const uint32_t* w, const DecodeConsts& k, uint32_t magic) {
   u32x4 r;
   if constexpr (BITS == 4) {
     const uint32_t x = w[KB];
-    r[0] = (x & k.m4lo) | k.magic;
-    r[1] = ((x >> 4) & k.m4lo) | k.magic;
-    r[2] = ((x >> 8) & k.m4lo) | k.magic;
-    r[3] = ((x >> 12) & k.m4lo) | k.magic;
+    r[0] = (x & k.m4lo) | magic;
+    r[1] = ((x >> 4) & k.m4lo) | magic;
+    r[2] = ((x >> 8) & k.m4lo) | magic;
+    r[3] = ((x >> 12) & k.m4lo) | magic;
   } else if constexpr (BITS == 2) {
     const uint32_t x = w[KB / 2];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) r[q] = ((x >> (2 * (4 * (KB % 2) + q))) & k.m2[0]) | k.magic;
+    for (int q = 0; q < 4; ++q) r[q] = ((x >> (2 * (4 * (KB % 2) + q))) & k.m2[0]) | magic;
   } else {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -221,10 +232,14 @@ __device__ inline u32x4 biased_frag(const uint32_t* w, const DecodeConsts& k) {
         case 12: f = pair6<12>(w); break; case 13: f = pair6<13>(w); break;
         case 14: f = pair6<14>(w); break; default: f = pair6<15>(w); break;
       }
-      r[q] = (f & 7u) | ((f & 0x38u) << 13) | k.magic;
+      r[q] = (f & 7u) | ((f & 0x38u) << 13) | magic;
     }
   }
   return r;
+}
+template <int BITS, int KB>
+__device__ inline u32x4 biased_frag(const uint32_t* w, const DecodeConsts& k) {
+  return biased_frag<BITS, KB>(w, k, k.magic);
 }
 
 // Fine zero-points, scale applied later: B operand RN_dt(q - z) for k-block KB,
@@ -347,11 +362,33 @@ __device__ inline u32x4 exact_frag(const uint32_t* w, const ExactParams& p, cons
 #pragma unroll
     for (int q = 0; q < 4; ++q) r[q] = as_u32(as_h2(t[q]) * p.s_h);
   } else if constexpr (MODE == LUT) {
+    // fp16 table values widened inside v_fma_mix: s * T exact in fp32 (adding
+    // -0 keeps the product's sign), one rounding to bf16
     const u32x4 t = table_frag<BITS, KB>(w, tab);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const h2 v = as_h2(t[q]);
-      r[q] = pack2<DT>(p.s * (float)v[0], p.s * (float)v[1]);
+      r[q] = pack2<DT>(__builtin_fmaf((float)v[0], p.s, k.nzero), __builtin_fmaf((float)v[1], p.s, k.nzero));
+    }
+  } else if constexpr (DT == BF16) {
+    // Codes decoded as fp16 (1024 + q) pairs, widened inside v_fma_mix:
+    //   integer zero-points: s * (1024 + q) - s * (1024 + z) = s * (q - z),
+    //     every term exact in fp32 (at most 22 significant bits);
+    //   fp16 zero-points: s * (1024 + q) - 1024 s = s * q exactly, then
+    //     minus s * z (exact) rounds once to the exact s * (q - z);
+    // then one rounding to bf16.
+    const u32x4 o = biased_frag<BITS, KB>(w, k, k.magic_h);
+    constexpr bool INT_Z = MODE == SYM || MODE == ZERO_PACKED;
+    const float c = INT_Z ? -__builtin_fmaf(1024.0f, p.s, p.sz) : -1024.0f * p.s;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const h2 v = as_h2(o[q]);
+      float lo = __builtin_fmaf((float)v[0], p.s, c), hi = __builtin_fmaf((float)v[1], p.s, c);
+      if constexpr (!INT_Z) {
+        lo -= p.sz;
+        hi -= p.sz;
+      }
+      r[q] = pack2<DT>(lo, hi);
     }
   } else {
     constexpr bool TL = false;

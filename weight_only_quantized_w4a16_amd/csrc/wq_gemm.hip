@@ -431,11 +431,16 @@ __global__ __launch_bounds__(256) void ksplit_reduce_kernel(const float* __restr
 template <int DT, int BITS, int MODE, int GPU, bool EPI>
 wq_status run_gemm(GemmArgs g, hipStream_t s) {
   // 128-row tiles unless that leaves fewer than about two workgroups per CU
-  // (a K split always runs 64-row tiles).  Modes whose decode needs more
-  // registers (fp16 zero-points, tables) run 64-row tiles: at 128 rows they
-  // spill (or drop to one wave per SIMD), which measured slower than decoding
-  // each weight for half as many rows.
-  constexpr bool HEAVY = MODE == ZERO_F16 || MODE == LUT || MODE == ZFINE;
+  // (a K split always runs 64-row tiles), and only for the decodes whose
+  // 128-row variant fits the 256 registers of a lane without spilling:
+  // symmetric 3- and 4-bit codes (4-bit with at most two groups per 128
+  // rows) and 3-bit integer zero-points with one group per 128 rows.  The
+  // others (fp16 zero-points, tables, fine zero-points, 2-bit codes, ...)
+  // spill at 128 rows, which measured up to 2.8x slower than decoding each
+  // weight for half as many rows.
+  constexpr bool FIT128 = (MODE == SYM && BITS != 2 && (BITS == 3 || GPU <= 2)) ||
+                          (MODE == ZERO_PACKED && BITS == 3 && GPU == 1);
+  constexpr bool HEAVY = !FIT128;
   g.ntiles_wg = (g.N + 255) / 256;
   const int bm =
       (HEAVY || g.ksplit > 1 || g.M <= 64 || (long)((g.M + 127) / 128) * g.ntiles_wg < 480) ? 64 : 128;
