@@ -20,7 +20,8 @@ Also reported:
                 against HBM bandwidth: its launches timed back to back over the
                 rotated copies between HIP events on its stream;
   gemm          the prefill layer set at M = 2048 (symmetric int4, group -1 and
-                128) through wq_gemm, as TFLOP/s against dense fp16 MFMA peak;
+                128) through wq_gemm, as TFLOP/s against dense fp16 MFMA peak
+                (each layer's launches graph-replayed; eager steps beside it);
   fused_gate_up the gate+up layer at M = 1 and 2048: plain product, plain
                 product + torch SiLU/multiply, and the fused SiLU(gate)*up
                 entry points;
@@ -432,13 +433,9 @@ def main():
             gy = [torch.empty((Mg, L.N), dtype=torch.float16, device=dev) for L in gl]
             flops = sum(2.0 * Mg * L.N * L.K for L in gl)
 
-            def gstep(i, ev=None):
+            def gstep(i):
                 for j in range(len(gl)):
-                    if ev is not None:
-                        ev[j][0].record(stream)
                     wq.wq_gemm(gx[j], gp[j][i % 2], out=gy[j], stream=stream)
-                    if ev is not None:
-                        ev[j][1].record(stream)
 
             for i in range(3):
                 gstep(i)
@@ -450,15 +447,38 @@ def main():
                 gstep(i)
             a1.record(stream)
             torch.cuda.synchronize()
-            gms = a0.elapsed_time(a1) / args.gemm_steps
+            eager_ms = a0.elapsed_time(a1) / args.gemm_steps
+            # each layer's launches (alternating copies) captured in a graph and
+            # replayed: GPU time per launch, median of 5 replays
+            layer_us = []
+            for j in range(len(gl)):
+                n = 2 * max(1, args.gemm_steps // 2)
+                gg = torch.cuda.CUDAGraph()
+                cap.wait_stream(stream)
+                with torch.cuda.stream(cap):
+                    with torch.cuda.graph(gg, stream=cap):
+                        for i in range(n):
+                            wq.wq_gemm(gx[j], gp[j][i % 2], out=gy[j], stream=cap)
+                    gg.replay()
+                stream.wait_stream(cap)
+                torch.cuda.synchronize()
+                ts = []
+                for _ in range(5):
+                    with torch.cuda.stream(cap):
+                        a0.record(cap)
+                        gg.replay()
+                        a1.record(cap)
+                    torch.cuda.synchronize()
+                    ts.append(a0.elapsed_time(a1) / n * 1e3)
+                layer_us.append(sorted(ts)[2])
+                del gg
+            gms = sum(layer_us) * 1e-3
             tflops = flops / (gms * 1e-3) / 1e12
-            gev = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in gl]
-            gstep(0, gev)
-            torch.cuda.synchronize()
             gemm[f"group_{gs}"] = {
                 "M": Mg, "ms_per_step": round(gms, 4), "tflops": round(tflops, 1),
                 "peak_tflops": MFMA_F16_PEAK_TFLOPS, "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
-                "per_layer_tflops": {L.name.split("/")[-1]: round(2.0 * Mg * L.N * L.K / (gev[j][0].elapsed_time(gev[j][1]) * 1e-3) / 1e12, 1)
+                "eager_ms_per_step": round(eager_ms, 4),
+                "per_layer_tflops": {L.name.split("/")[-1]: round(2.0 * Mg * L.N * L.K / (layer_us[j] * 1e-6) / 1e12, 1)
                                      for j, L in enumerate(gl)}}
             del gp, gx, gy
             torch.cuda.empty_cache()
