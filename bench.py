@@ -190,7 +190,7 @@ def run_points(args):
                         has_perm = copies[0].perm is not None
                         ws = torch.empty(max(wq.wq_workspace_bytes(M, N, K, bits, has_perm), 16),
                                          dtype=torch.uint8, device=dev)
-                        path = "gemv" if M <= wq.GEMV_MAX_M else "gemm"
+                        path = "gemv" if wq.use_gemv(M, copies[0]) else "gemm"
                         n = R * max(1, -(-8 // R))
                         us = graph_time(lambda i: wq.linear(x, copies[i % R], out=y, ws=ws, stream=s), n)
                         flops = 2.0 * M * N * K

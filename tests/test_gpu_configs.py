@@ -64,7 +64,7 @@ def test_config_parity(orc, wq, cid, lname, bits, gs, M):
     L, layer = get_layer(wq, cfg, lname, bits, gs)
     x_bits = cfg.x(M, L.K)
     x = bits_to_tensor(x_bits, act_dtype(cfg.dtype), "cuda")
-    fn = wq.wq_gemv if M <= wq.GEMV_MAX_M else wq.wq_gemm
+    fn = wq.wq_gemv if wq.use_gemv(M, layer) else wq.wq_gemm
     y = fn(x, layer)
     torch.cuda.synchronize()
     if L.N * M <= 4096 * 16:

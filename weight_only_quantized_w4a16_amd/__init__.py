@@ -219,16 +219,24 @@ def wq_hadamard(x: torch.Tensor, block: int, out: Optional[torch.Tensor] = None,
 
 
 # Largest M that linear() sends to wq_gemv (which takes M <= 32).  Measured on
-# MI355X over the LLaMA-7B/70B/405B layer shapes: two blocks of 16 activation
-# rows beat the tiled GEMM up to M = 24 on every shape, and lose to it on the
-# wide and long-K shapes by M = 32.
-GEMV_MAX_M = 24
+# MI355X over the LLaMA-7B/70B/405B layer shapes (graph-replayed, rotated
+# copies): the GEMV beats the tiled GEMM at M = 24 and 32 on every shape and
+# code width, except 2-bit table layers above 16 rows, whose second block of
+# rows takes a second pass over the weights.
+GEMV_MAX_M = 32
+
+
+def use_gemv(M: int, layer: PackedLayer) -> bool:
+    """Whether linear() sends an M-row product with this layer to the GEMV."""
+    if layer.bits == 2 and layer.mode == LUT:
+        return M <= 16
+    return M <= GEMV_MAX_M
 
 
 def linear(x: torch.Tensor, layer: PackedLayer, out=None, ws=None, stream=None) -> torch.Tensor:
-    """M <= GEMV_MAX_M goes to wq_gemv, larger M to wq_gemm (the *_gate_up pair for
-    a layer from wq_repack_gate_up)."""
-    small = x.shape[0] <= GEMV_MAX_M
+    """Decode-sized M (use_gemv) goes to wq_gemv, larger M to wq_gemm (the
+    *_gate_up pair for a layer from wq_repack_gate_up)."""
+    small = use_gemv(x.shape[0], layer)
     if layer.gate_up:
         return (wq_gemv_gate_up if small else wq_gemm_gate_up)(x, layer, out, ws, stream)
     return (wq_gemv if small else wq_gemm)(x, layer, out, ws, stream)

@@ -81,12 +81,21 @@ __device__ inline float zero_corr(float z) {
 template <int BITS, int TN, int GPU, int MR>
 constexpr bool gemv_big_frames() { return TN >= 4 || BITS == 2 || (TN >= 2 && GPU >= 4) || MR >= 2; }
 
+// LDS bytes per wave: the partial results of the cross-wave reduction, or,
+// in the standard scheme, at least the 4 KiB activation stage (the same bytes
+// serve both, one after the other).
+template <int TN, int MR, bool PACKED, bool STAGE>
+constexpr int gemv_wave_lds() {
+  constexpr int red = TN * MR * (PACKED ? 1 : 4) * 64 * 4;
+  return STAGE && red < 4096 ? 4096 : red;
+}
+
 // SWIGLU: the layer is a fused gate+up layer repacked with interleaved column
 // tiles (gate, up, gate, up, ...).  Workgroup p owns output tile p: its even
 // waves stream gate tile 2p, its odd waves up tile 2p + 1 (TN = 1, each pair
 // of waves shares one k-range), and the store writes SiLU(gate) * up.
 // MR: blocks of 16 activation rows (standard scheme; M <= 16 MR).
-template <int DT, int BITS, int MODE, int TN, int GPU, bool PACKED, int PF, bool SWIGLU, int MR>
+template <int DT, int BITS, int MODE, int TN, int GPU, bool PACKED, int PF, bool SWIGLU, int MR, bool STAGE>
 __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU, MR>() ? 512 : 1024)) void gemv_kernel(const GemvArgs a) {
   constexpr int KT = BITS == 2 ? 256 : 128;
   constexpr int UPT = KT / 128;                 // 128-row units per tile
@@ -106,7 +115,12 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU, MR>() ? 512 : 1024)
   constexpr int NRED = PACKED ? 1 : 4;          // reduced values per lane per column tile
 
   __shared__ uint32_t table[TABLE ? (32 << (2 * BITS)) : 1];
-  extern __shared__ float red[];                // [waves][TN][MR][NRED][64]
+  // LDS of wave w at red + w * WSTRIDE: its activation stage (standard scheme,
+  // 4 KiB) while it streams, then its partial results [TN][MR][NRED][64] for
+  // the cross-wave reduction.
+  extern __shared__ float red[];
+  constexpr int WSTRIDE = gemv_wave_lds<TN, MR, PACKED, STAGE>() / 4;  // floats
+  static_assert(!STAGE || !PACKED, "the packed scheme loads its fragments directly");
   static_assert(!PACKED || MR == 1, "the packed scheme holds at most 4 rows");
 
   const int lane = threadIdx.x & 63;
@@ -123,13 +137,32 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU, MR>() ? 512 : 1024)
   // Buffer offsets = per-lane vector part + per-tile scalar part.  The vector
   // part becomes kOutOfRange for loads that must return zero (rows past M,
   // tiles past the wave's range).
-  //   packed:   lane c -> (m = c / 4, k-block c % 4) ; standard: lane c -> m = 16 r + c
-  uint32_t x_lane[MR];
+  //   packed:   lane c -> (m = c / 4, k-block c % 4), one load per 128-row unit;
+  //   standard: lane c -> m = 16 r + c, one load per k-block (the MFMA
+  //             fragment itself: 16 rows, half a cache line each, per load);
+  //   staged:   load j of a unit and row block r reads rows 16 r + 4 j .. + 3,
+  //             lane L -> row 16 r + 4 j + L / 16, 16 bytes at k = 8 (L % 16):
+  //             four rows x 256 contiguous bytes per load, regrouped into
+  //             MFMA fragments through the wave's LDS stage.
+  constexpr int XJ = STAGE ? 4 : 1;
+  uint32_t x_lane[MR][XJ];
 #pragma unroll
-  for (int r = 0; r < MR; ++r) {
-    const int xm = PACKED ? (c >> 2) : 16 * r + c;
-    x_lane[r] = xm < a.M ? (uint32_t)(xm * a.K + 8 * h + (PACKED ? 32 * (c & 3) : 0)) * 2u : kOutOfRange;
-  }
+  for (int r = 0; r < MR; ++r)
+#pragma unroll
+    for (int j = 0; j < XJ; ++j) {
+      const int xm = PACKED ? (c >> 2) : STAGE ? 16 * r + 4 * j + h : 16 * r + c;
+      const int xk = PACKED ? 8 * h + 32 * (c & 3) : STAGE ? 8 * c : 8 * h;
+      x_lane[r][j] = xm < a.M ? (uint32_t)(xm * a.K + xk) * 2u : kOutOfRange;
+    }
+  // LDS stage of this wave: row i (0..15) of the unit at 16 chunks of 16 bytes,
+  // chunk q stored at position q ^ i (the fragment reads of 16 rows then hit
+  // 16 different bank groups)
+  u32x4* const stage = (u32x4*)(red + (size_t)wave * WSTRIDE);
+  int st_w[XJ], st_r[4];
+#pragma unroll
+  for (int j = 0; j < XJ; ++j) st_w[j] = (4 * j + h) * 16 + (c ^ (4 * j + h));
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) st_r[kb] = c * 16 + ((4 * kb + h) ^ c);
   const uint32_t w_lane = (uint32_t)lane * WPL * 4;
   const uint32_t s_lane = (uint32_t)c * REC;
   const uint32_t zp_lane = (uint32_t)(c >> 3) * ZREC;
@@ -168,11 +201,12 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU, MR>() ? 512 : 1024)
     }
 #pragma unroll
     for (int r = 0; r < MR; ++r) {
-      const uint32_t xv = ok ? x_lane[r] : kOutOfRange;
 #pragma unroll
       for (int i = 0; i < NXA; ++i) {
-        // packed: unit i covers rows 128 i ..; standard: k-block i covers rows 32 i ..
-        const uint32_t koff = (uint32_t)(ktc * KT + (PACKED ? 128 * i : 32 * i)) * 2u;
+        // packed: load i covers unit i; standard: k-block i; staged: load
+        // j = i % 4 of unit i / 4
+        const uint32_t xv = ok ? x_lane[r][STAGE ? i % 4 : 0] : kOutOfRange;
+        const uint32_t koff = (uint32_t)(ktc * KT + (PACKED ? 128 * i : STAGE ? 128 * (i / 4) : 32 * i)) * 2u;
         f.xa[r][i] = __builtin_amdgcn_raw_buffer_load_b128(rx, xv, koff, 0);
       }
     }
@@ -250,6 +284,21 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU, MR>() ? 512 : 1024)
           }
         }
       } else {
+        // the unit's activations as MFMA fragments (k-block kb: rows 16 r + c,
+        // k = 32 kb + 8 h ..), regrouped through the LDS stage when staged
+        u32x4 xf[MR][4];
+#pragma unroll
+        for (int r = 0; r < MR; ++r) {
+          if constexpr (STAGE) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) stage[st_w[j]] = f.xa[r][4 * u + j];
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) xf[r][kb] = stage[st_r[kb]];
+          } else {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) xf[r][kb] = f.xa[r][4 * u + kb];
+          }
+        }
         sfor<GPU>([&](auto gc) {
           constexpr int gi = decltype(gc)::value;
           f4 acc[MR][TN];
@@ -268,11 +317,11 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU, MR>() ? 512 : 1024)
                   f.w[t], tab, dk, FINE ? fine_zero_bits(f.z[t][u], kb - 4 * u) : 0u,
                   SCALED ? rec_scale<Z16>(f.s[t][u], gi) : 0.0f);
 #pragma unroll
-              for (int r = 0; r < MR; ++r) acc[r][t] = mfma16<DT>(f.xa[r][kb], b, acc[r][t]);
+              for (int r = 0; r < MR; ++r) acc[r][t] = mfma16<DT>(xf[r][kb - 4 * u], b, acc[r][t]);
             }
             if constexpr (XS)
 #pragma unroll
-              for (int r = 0; r < MR; ++r) xs[r] = mfma16<DT>(f.xa[r][kb], ones_frag<DT>(), xs[r]);
+              for (int r = 0; r < MR; ++r) xs[r] = mfma16<DT>(xf[r][kb - 4 * u], ones_frag<DT>(), xs[r]);
           });
 #pragma unroll
           for (int t = 0; t < TN; ++t) {
@@ -316,7 +365,7 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU, MR>() ? 512 : 1024)
   for (int t = 0; t < TN; ++t)
 #pragma unroll
     for (int r = 0; r < MR; ++r) {
-      float* dst = red + ((size_t)((wave * TN + t) * MR + r) * NRED) * 64;
+      float* dst = red + (size_t)wave * WSTRIDE + (size_t)((t * MR + r) * NRED) * 64;
       if constexpr (PACKED) {
         dst[lane] = (tot[r][t][0] + tot[r][t][1]) + (tot[r][t][2] + tot[r][t][3]);
       } else {
@@ -332,7 +381,7 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU, MR>() ? 512 : 1024)
     // sum over the waves w0, w0 + step, ... of tile t's partial results
     auto reduce = [&](int w0, int step) {
       float v = 0.0f;
-      for (int w = w0; w < a.waves; w += step) v += red[((size_t)((w * TN + t) * MR + rb) * NRED + e) * 64 + l];
+      for (int w = w0; w < a.waves; w += step) v += red[(size_t)w * WSTRIDE + ((t * MR + rb) * NRED + e) * 64 + l];
       return v;
     };
     float v;
@@ -352,11 +401,10 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU, MR>() ? 512 : 1024)
 // ---------------------------------------------------------------------------
 // Launch-shape choice and dispatch.
 // ---------------------------------------------------------------------------
-template <int DT, int BITS, int MODE, int TN, int GPU, bool PACKED, int PF, bool SWIGLU, int MR>
+template <int DT, int BITS, int MODE, int TN, int GPU, bool PACKED, int PF, bool SWIGLU, int MR, bool STAGE>
 wq_status run(GemvArgs g, int grid, hipStream_t s) {
-  constexpr int NRED = PACKED ? 1 : 4;
-  const size_t lds = (size_t)g.waves * TN * MR * NRED * 64 * sizeof(float);
-  hipLaunchKernelGGL((gemv_kernel<DT, BITS, MODE, TN, GPU, PACKED, PF, SWIGLU, MR>), dim3(grid), dim3(g.waves * 64),
+  const size_t lds = (size_t)g.waves * gemv_wave_lds<TN, MR, PACKED, STAGE>();
+  hipLaunchKernelGGL((gemv_kernel<DT, BITS, MODE, TN, GPU, PACKED, PF, SWIGLU, MR, STAGE>), dim3(grid), dim3(g.waves * 64),
                      lds, s, g);
   return launch_status();
 }
@@ -374,17 +422,29 @@ inline int pick_waves(int grid, int ktiles, bool table, int wmax) {
   while (w < wmax && 2 * w <= ktiles && ((long)grid * w < target || ktiles > 32 * w)) w *= 2;
   return w;
 }
-template <int DT, int BITS, int MODE, int TN, int GPU, bool PACKED, bool SWIGLU, int MR>
+template <int DT, int BITS, int MODE, int TN, int GPU, bool PACKED, bool SWIGLU, int MR, bool STAGE = false>
 wq_status run_pf(GemvArgs g, int grid, hipStream_t s) {
   const int tpw = g.kt_per_wave;
   if constexpr (PACKED) {
-    if (tpw >= 8) return run<DT, BITS, MODE, TN, GPU, PACKED, 4, SWIGLU, MR>(g, grid, s);
-    if (tpw >= 5) return run<DT, BITS, MODE, TN, GPU, PACKED, 3, SWIGLU, MR>(g, grid, s);
+    if (tpw >= 8) return run<DT, BITS, MODE, TN, GPU, PACKED, 4, SWIGLU, MR, false>(g, grid, s);
+    if (tpw >= 5) return run<DT, BITS, MODE, TN, GPU, PACKED, 3, SWIGLU, MR, false>(g, grid, s);
   }
-  return run<DT, BITS, MODE, TN, GPU, PACKED, 2, SWIGLU, MR>(g, grid, s);
+  return run<DT, BITS, MODE, TN, GPU, PACKED, 2, SWIGLU, MR, STAGE>(g, grid, s);
 }
 
 // Standard scheme (one activation row per MFMA row, MR blocks of 16 rows).
+// Activations go through the LDS stage for more than 8 rows (measured on the
+// decode layer shapes: 5-38 % faster at 16 rows, up to 5 % slower at 5),
+// except with four column tiles per wave and table codes, whose LDS table
+// and stage together cost occupancy.
+template <int DT, int BITS, int MODE, int TN, int GPU, bool SWIGLU, int MR>
+wq_status run_standard(GemvArgs g, int grid, hipStream_t s) {
+  const bool stage = MR == 2 || (g.M > 8 && !(MODE == LUT && TN == 4));
+  if constexpr (MR == 1)
+    if (!stage) return run_pf<DT, BITS, MODE, TN, GPU, false, SWIGLU, MR, false>(g, grid, s);
+  return run_pf<DT, BITS, MODE, TN, GPU, false, SWIGLU, MR, true>(g, grid, s);
+}
+
 template <int DT, int BITS, int MODE, int GPU, bool SWIGLU, int MR>
 wq_status pick_standard(GemvArgs g, hipStream_t s) {
   const int ntiles = g.N / 16;
@@ -398,26 +458,29 @@ wq_status pick_standard(GemvArgs g, hipStream_t s) {
     const int kw = max(1, pick_waves(ntiles, g.ktiles, MODE == LUT, wmax) / 2);  // waves per column tile
     g.waves = 2 * kw;
     g.kt_per_wave = (g.ktiles + kw - 1) / kw;
-    return run_pf<DT, BITS, MODE, 1, GPU, false, true, MR>(g, ntiles / 2, s);
+    return run_standard<DT, BITS, MODE, 1, GPU, true, MR>(g, ntiles / 2, s);
   } else {
     // Each wave loads 16 activation rows per row block and k-tile -- up to four
     // times the weight bytes of a column tile -- so wide layers give a wave
     // four (or two) column tiles that share those loads; narrow layers keep one
     // so that enough workgroups run.
-    int tn = ntiles >= 768 ? 4 : ntiles >= 512 ? 2 : 1;
     // 2-bit frames hold 256 rows, and a second row block doubles the activation
-    // frames: four tiles would not fit the registers
-    if ((BITS == 2 || MR == 2) && tn > 2) tn = 2;
+    // frames: four tiles would not fit the registers (nor two, for 2-bit codes
+    // with four groups per 128 rows)
+    constexpr int TNMAX = (BITS == 2 && GPU == 4) ? 1 : (BITS == 2 || MR == 2) ? 2 : 4;
+    int tn = ntiles >= 768 ? 4 : ntiles >= 512 ? 2 : 1;
+    if (tn > TNMAX) tn = TNMAX;
     while (ntiles % tn != 0) tn /= 2;
     const int grid = ntiles / tn;
     const bool big = tn == 4 ? gemv_big_frames<BITS, 4, GPU, MR>()
                    : tn == 2 ? gemv_big_frames<BITS, 2, GPU, MR>() : gemv_big_frames<BITS, 1, GPU, MR>();
     g.waves = pick_waves(grid, g.ktiles, MODE == LUT, big ? 8 : 16);
     g.kt_per_wave = (g.ktiles + g.waves - 1) / g.waves;
-    if constexpr (BITS != 2 && MR == 1)
-      if (tn == 4) return run_pf<DT, BITS, MODE, 4, GPU, false, false, MR>(g, grid, s);
-    if (tn == 2) return run_pf<DT, BITS, MODE, 2, GPU, false, false, MR>(g, grid, s);
-    return run_pf<DT, BITS, MODE, 1, GPU, false, false, MR>(g, grid, s);
+    if constexpr (TNMAX >= 4)
+      if (tn == 4) return run_standard<DT, BITS, MODE, 4, GPU, false, MR>(g, grid, s);
+    if constexpr (TNMAX >= 2)
+      if (tn == 2) return run_standard<DT, BITS, MODE, 2, GPU, false, MR>(g, grid, s);
+    return run_standard<DT, BITS, MODE, 1, GPU, false, MR>(g, grid, s);
   }
 }
 

@@ -24,7 +24,7 @@ from typing import List, Optional
 
 import torch
 
-from . import GEMV_MAX_M, PackedLayer, wq_gemv, wq_gemv_gate_up, wq_gemm, wq_gemm_gate_up
+from . import PackedLayer, use_gemv, wq_gemv, wq_gemv_gate_up, wq_gemm, wq_gemm_gate_up
 
 
 @dataclasses.dataclass
@@ -54,7 +54,7 @@ class DecodeStack:
                 raise ValueError("the QKV output must hold at least dim columns")
         self.layers = layers
         self.M = M
-        small = M <= GEMV_MAX_M
+        small = all(use_gemv(M, lay) for L in layers for lay in (L.qkv, L.o, L.gate_up, L.down))
         self._lin = wq_gemv if small else wq_gemm
         self._lin_gu = wq_gemv_gate_up if small else wq_gemm_gate_up
         e = dict(dtype=dtype, device=device)
