@@ -67,7 +67,7 @@ def test_packed_bytes_matches_layout(L):
 
 def test_workspace_bytes(L):
     al = lambda v: (v + 255) // 256 * 256
-    # 2 x 16 workgroups of 64 x 256 -> 16 slices wanted, capped at 4 k-tiles per slice
+    # 2 x 16 workgroups of 64 x 256 -> 16 slices allowed, capped at 4 k-tiles per slice
     assert L.wq_workspace_bytes(128, 4096, 4096, 4, 0) == 8 * 128 * 4096 * 4
     assert L.wq_workspace_bytes(128, 4096, 4096, 4, 1) == al(128 * 4096 * 2) + 8 * 128 * 4096 * 4
     # 8 x 16 workgroups -> 4 slices of 22 (last 20) k-tiles
@@ -75,12 +75,12 @@ def test_workspace_bytes(L):
     assert L.wq_workspace_bytes(65, 53248, 16384, 4, 0) == 0         # 416 workgroups: no split
     assert L.wq_workspace_bytes(4096, 4096, 4096, 4, 0) == 0
     assert L.wq_workspace_bytes(128, 4096, 4096, 4, 1) > L.wq_workspace_bytes(128, 4096, 4096, 4, 0)
-    # narrow problems split K: 16 workgroups of 256 columns -> 32 slices wanted,
+    # narrow problems split K: 16 workgroups of 256 columns -> 32 slices allowed,
     # capped at 4 k-tiles per slice (32 k-tiles -> 8 slices)
     assert L.wq_workspace_bytes(16, 4096, 4096, 4, 0) == 8 * 16 * 4096 * 4
     assert L.wq_workspace_bytes(16, 4096, 4096, 4, 1) == al(16 * 4096 * 2) + 8 * 16 * 4096 * 4
-    # 208 workgroups -> 3 slices of 43 (last 42) k-tiles
-    assert L.wq_workspace_bytes(32, 53248, 16384, 4, 0) == 3 * 32 * 53248 * 4
+    # 208 workgroups -> 2 slices of 64 k-tiles (a third would exceed 512 workgroups)
+    assert L.wq_workspace_bytes(32, 53248, 16384, 4, 0) == 2 * 32 * 53248 * 4
     # wide enough: no split
     assert L.wq_workspace_bytes(64, 131072, 4096, 4, 0) == 0
 

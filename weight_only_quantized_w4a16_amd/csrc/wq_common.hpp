@@ -41,13 +41,15 @@ inline wq_status check_layer(int K, int N, int bits, int group_size, int mode) {
 // K split of the large-M product.  A workgroup covers 256 columns and 64 rows
 // when the grid is small, so a narrow layer at moderate M (fewer such
 // workgroups than CUs) leaves most of the GPU idle; its K range is then split
-// until about 512 workgroups run, keeping at least 4 k-tiles per split.  The
-// partial products go through an fp32 workspace.
+// into as many slices as keep the grid within 512 workgroups (one round at two
+// workgroups per CU: rounding up left a few workgroups for a second round,
+// 18 % slower on the 70B table layer at M = 64), at least 4 k-tiles per
+// slice.  The partial products go through an fp32 workspace.
 inline int gemm_ksplit(int M, int N, int K, int bits) {
   const long nwg = (long)((M + 63) / 64) * ((N + 255) / 256);  // 64 x 256 workgroups
   if (nwg >= 256) return 1;
   const int ktiles = K / tile_k(bits);
-  int s = (int)((512 + nwg - 1) / nwg);
+  int s = (int)(512 / nwg);  // at most 512: one round at two workgroups per CU
   if (s > ktiles / 4) s = ktiles / 4;
   if (s <= 1) return 1;
   const int per = (ktiles + s - 1) / s;  // k-tiles per split; no split left empty

@@ -21,7 +21,9 @@
 //    x*B are exact in fp32 and the bias cancels in the correction.
 //  * M <= 4 packs (row m, k-block kb) into MFMA row 4m + kb, so one 128-bit
 //    activation load feeds the 4 k-blocks of a unit; larger M uses one MFMA
-//    row per activation row and one activation load per k-block.
+//    row per activation row (blocks of 16 rows, two for M > 16), loading
+//    either the fragments themselves (M <= 8) or four rows x 256 contiguous
+//    bytes per load, regrouped into fragments through a per-wave LDS stage.
 //  * Waves reduce through LDS at the end; the output is rounded once.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
