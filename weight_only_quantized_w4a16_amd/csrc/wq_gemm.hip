@@ -385,18 +385,20 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
 
 // Sum of the K-split partial products, rounded once to the activation dtype
 // (y [M][N]), or, for a fused gate+up layer, SiLU(gate) * up of the summed
-// halves (y [M][N/2]; partial columns in the interleaved tile order).  A
-// workgroup covers 32 groups of 4 consecutive outputs; its 8 thread rows sum
-// every 8th slice (all their loads independent, so in flight together) and
-// thread row 0 adds the 8 row sums in order: a fixed summation order.
+// halves (y [M][N/2]; partial columns in the interleaved tile order).  Each
+// group of 4 consecutive outputs has `rows` threads (1, 2, 4 or 8, more when
+// there are few outputs): thread row r sums slices r, r + rows, ... (all its
+// loads independent, so in flight together), then row 0 adds the row sums in
+// order: a fixed summation order for a given shape.
 template <int DT>
 __global__ __launch_bounds__(256) void ksplit_reduce_kernel(const float* __restrict__ part, int ksplit, int M, int N,
-                                                            int swiglu, uint16_t* __restrict__ y) {
-  __shared__ f4 red_g[8][32], red_u[8][32];
+                                                            int swiglu, int rows, uint16_t* __restrict__ y) {
+  __shared__ f4 red_g[256], red_u[256];
   const int ldy = swiglu ? N / 2 : N;
   const size_t quads = (size_t)M * ldy / 4;
-  const int ql = threadIdx.x & 31, row = threadIdx.x >> 5;
-  const size_t q = (size_t)blockIdx.x * 32 + ql;
+  const int qw = 256 / rows;  // groups of 4 outputs per workgroup
+  const int ql = threadIdx.x % qw, row = threadIdx.x / qw;
+  const size_t q = (size_t)blockIdx.x * qw + ql;
   const size_t slice = (size_t)M * N;
   f4 g = {0.0f, 0.0f, 0.0f, 0.0f}, u = g;
   int m = 0, j = 0;
@@ -405,27 +407,28 @@ __global__ __launch_bounds__(256) void ksplit_reduce_kernel(const float* __restr
     j = (int)(q * 4 % ldy);  // first of 4 outputs (ldy % 16 == 0)
     const int col = swiglu ? (j / 16) * 32 + j % 16 : j;  // gate column; up is 16 further
     const float* p = part + (size_t)m * N + col;
-    for (int k = row; k < ksplit; k += 8) {
+    for (int k = row; k < ksplit; k += rows) {
       g += *(const f4*)(p + k * slice);
       if (swiglu) u += *(const f4*)(p + k * slice + 16);
     }
   }
-  red_g[row][ql] = g;
-  red_u[row][ql] = u;
-  __syncthreads();
-  if (row != 0 || q >= quads) return;
-  f4 v = red_g[0][ql], w = red_u[0][ql];
-#pragma unroll
-  for (int r = 1; r < 8; ++r) {
-    v += red_g[r][ql];
-    w += red_u[r][ql];
+  if (rows > 1) {
+    red_g[threadIdx.x] = g;
+    red_u[threadIdx.x] = u;
+    __syncthreads();
+    if (row != 0) return;
+    for (int r = 1; r < rows; ++r) {
+      g += red_g[r * qw + ql];
+      u += red_u[r * qw + ql];
+    }
   }
+  if (q >= quads) return;
   if (swiglu) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = v[e] / (1.0f + expf(-v[e])) * w[e];
+    for (int e = 0; e < 4; ++e) g[e] = g[e] / (1.0f + expf(-g[e])) * u[e];
   }
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-  *(u32x2*)(y + (size_t)m * ldy + j) = u32x2{pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
+  *(u32x2*)(y + (size_t)m * ldy + j) = u32x2{pack2<DT>(g[0], g[1]), pack2<DT>(g[2], g[3])};
 }
 
 template <int DT, int BITS, int MODE, int GPU, bool EPI>
@@ -455,8 +458,11 @@ wq_status run_gemm(GemmArgs g, hipStream_t s) {
   }
   if (g.ksplit > 1) {
     const size_t quads = (size_t)g.M * (g.swiglu ? g.N / 2 : g.N) / 4;
-    hipLaunchKernelGGL((ksplit_reduce_kernel<DT>), dim3((unsigned)((quads + 31) / 32)), dim3(256), 0, s,
-                       (const float*)g.part, g.ksplit, g.M, g.N, g.swiglu, g.y);
+    int rows = 1;  // threads per group of 4 outputs: about 2^18 threads in all
+    while (rows < 8 && rows < g.ksplit && quads * rows < ((size_t)1 << 18)) rows *= 2;
+    const size_t qw = 256 / rows;
+    hipLaunchKernelGGL((ksplit_reduce_kernel<DT>), dim3((unsigned)((quads + qw - 1) / qw)), dim3(256), 0, s,
+                       (const float*)g.part, g.ksplit, g.M, g.N, g.swiglu, rows, g.y);
   }
   return launch_status();
 }
