@@ -204,6 +204,23 @@ def test_gemm_k_split_parity(orc, wq, mode, bits, dt, gs):
         check_product(orc, wq, "wq_gemm", L, M, dt, 123 + M)
 
 
+@pytest.mark.parametrize("M", [40, 64, 200])
+def test_gemm_k_split_reduction_rows(orc, wq, M):
+    """A 4096-column layer split into 4 slices, at row counts where the
+    reduction gives each group of 4 outputs 4 (M = 40, 64) or 2 (M = 200)
+    threads; the oracle computes a seeded sample of columns."""
+    K, N = 2048, 4096
+    assert wq.wq_workspace_bytes(M, N, K, 4, False) == 4 * M * N * 4
+    L = make(wl.ZERO_F16, 4, 128, K, N, 8800 + M)
+    layer = repack_layer(wq, L)
+    x_bits = wl.make_x(M, K, wl.F16, 5 + M)
+    y = wq.wq_gemm(bits_to_tensor(x_bits, torch.float16, "cuda"), layer)
+    torch.cuda.synchronize()
+    cols = np.unique(np.concatenate([wl.sample_cols(N, 160, seed=M), np.arange(N - 16, N)])).astype(np.int32)
+    ok, err, bound = within_tolerance(tensor_f64(y)[:, cols], oracle_y(orc, x_bits, wl.F16, L, cols))
+    assert ok, f"max error {err:.3e} > bound {bound:.3e}"
+
+
 def test_gemm_k_split_uneven_and_act_order(orc, wq):
     """K = 1664 (13 k-tiles) splits into slices of 4, 4, 4 and 1 tiles; with
     act-order the workspace holds the permuted activations and the partial
