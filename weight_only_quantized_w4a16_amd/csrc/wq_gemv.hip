@@ -97,6 +97,8 @@ constexpr int gemv_wave_lds() {
 // waves stream gate tile 2p, its odd waves up tile 2p + 1 (TN = 1, each pair
 // of waves shares one k-range), and the store writes SiLU(gate) * up.
 // MR: blocks of 16 activation rows (standard scheme; M <= 16 MR).
+// STAGE: standard scheme with contiguous activation loads regrouped through
+// the wave's LDS stage (otherwise the fragments are loaded directly).
 template <int DT, int BITS, int MODE, int TN, int GPU, bool PACKED, int PF, bool SWIGLU, int MR, bool STAGE>
 __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU, MR>() ? 512 : 1024)) void gemv_kernel(const GemvArgs a) {
   constexpr int KT = BITS == 2 ? 256 : 128;
