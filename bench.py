@@ -719,8 +719,14 @@ def main():
             if time.perf_counter() - t0 >= args.cpu_seconds or reps >= 50:
                 break
         dt = time.perf_counter() - t0
+        model = ""
+        try:
+            with open("/proc/cpuinfo") as fh:
+                model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "")
+        except OSError:
+            pass
         cpu = {"value": round(reps * set_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
-               "kind": "oracle",
+               "cpu_model": model, "kind": "oracle",
                "sample": f"{reps} full passes of the decode layer set (M=1, all columns) in {dt:.1f} s"}
 
     out = {
