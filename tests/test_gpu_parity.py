@@ -117,6 +117,28 @@ def test_gemv_wide_two_row_blocks(orc, wq, mode, bits):
         assert ok, f"max error {err:.3e} > bound {bound:.3e}"
 
 
+TILE128_CASES = [(wl.SYM, 4, 128), (wl.SYM, 4, 64), (wl.SYM, 3, -1), (wl.ZERO_F16, 4, 128), (wl.ZERO_F16, 3, 256),
+                 (wl.ZERO_PACKED, 3, 128), (wl.LUT, 3, 64)]
+
+
+@pytest.mark.parametrize("mode,bits,gs", TILE128_CASES)
+@pytest.mark.parametrize("dt", [wl.F16, wl.BF16])
+def test_gemm_128_row_tiles(orc, wq, mode, bits, gs, dt):
+    """Enough row and column blocks (9 x 61 >= 480) for the 128-row tiles of
+    the decodes that have them; the last row tile and the last column block
+    are ragged.  The oracle computes a seeded sample of columns."""
+    K, N, M = 512, 15520, 1088
+    L = make(mode, bits, gs, K, N, 9100 + 7 * mode + bits + dt)
+    layer = repack_layer(wq, L)
+    x_bits = wl.make_x(M, K, dt, 17 + mode + bits)
+    print(f"[gemm 128-row] mode={mode} bits={bits} gs={gs} dt={dt}", flush=True)
+    y = wq.wq_gemm(bits_to_tensor(x_bits, act_dtype(dt), "cuda"), layer)
+    torch.cuda.synchronize()
+    cols = np.unique(np.concatenate([wl.sample_cols(N, 96, seed=mode + bits), np.arange(N - 16, N)])).astype(np.int32)
+    ok, err, bound = within_tolerance(tensor_f64(y)[:, cols], oracle_y(orc, x_bits, dt, L, cols))
+    assert ok, f"max error {err:.3e} > bound {bound:.3e}"
+
+
 def test_m_zero_is_a_noop(wq):
     L = make(wl.SYM, 4, 128, 512, 64, 5)
     layer = repack_layer(wq, L)

@@ -435,14 +435,19 @@ template <int DT, int BITS, int MODE, int GPU, bool EPI>
 wq_status run_gemm(GemmArgs g, hipStream_t s) {
   // 128-row tiles unless that leaves fewer than about two workgroups per CU
   // (a K split always runs 64-row tiles), and only for the decodes whose
-  // 128-row variant fits the 256 registers of a lane without spilling:
-  // symmetric 3- and 4-bit codes (4-bit with at most two groups per 128
-  // rows) and 3-bit integer zero-points with one group per 128 rows.  The
-  // others (fp16 zero-points, tables, fine zero-points, 2-bit codes, ...)
-  // spill at 128 rows, which measured up to 2.8x slower than decoding each
-  // weight for half as many rows.
+  // 128-row variant fits the 256 registers of a lane without spilling and
+  // keeps two workgroups per CU: symmetric 3- and 4-bit codes (4-bit with at
+  // most two groups per 128 rows), fp16 zero-points with one group per 128
+  // rows, 3-bit integer zero-points with one group per 128 rows, 3-bit tables
+  // (4-bit tables fit too, but their 32 KiB LDS table leaves one workgroup
+  // per CU: 8-12 % slower).  The others spill at 128 rows, up to 2.8x slower
+  // than decoding each weight for half as many rows.  Measured gains of the
+  // 128-row tiles at M = 2048-4096: 7-31 % on fp16 zero-points and 3-bit
+  // tables.
   constexpr bool FIT128 = (MODE == SYM && BITS != 2 && (BITS == 3 || GPU <= 2)) ||
-                          (MODE == ZERO_PACKED && BITS == 3 && GPU == 1);
+                          (MODE == ZERO_F16 && BITS != 2 && GPU == 1) ||
+                          (MODE == ZERO_PACKED && BITS == 3 && GPU == 1) ||
+                          (MODE == LUT && BITS == 3);
   constexpr bool HEAVY = !FIT128;
   g.ntiles_wg = (g.N + 255) / 256;
   const int bm =
