@@ -139,6 +139,33 @@ def test_gemm_128_row_tiles(orc, wq, mode, bits, gs, dt):
     assert ok, f"max error {err:.3e} > bound {bound:.3e}"
 
 
+NARROW_TILE_CASES = [(wl.SYM, 4, 32), (wl.SYM, 2, 128), (wl.ZERO_F16, 4, 64), (wl.ZERO_F16, 2, 256),
+                     (wl.ZERO_PACKED, 4, 128), (wl.ZERO_PACKED, 4, 32), (wl.ZERO_PACKED, 3, 64),
+                     (wl.ZERO_PACKED, 2, 256), (wl.LUT, 2, 64), (wl.ZERO_F16_G8, 4, -1), (wl.ZERO_F16_G32, 3, 128)]
+
+
+@pytest.mark.parametrize("mode,bits,gs", NARROW_TILE_CASES)
+@pytest.mark.parametrize("dt", [wl.F16, wl.BF16])
+def test_gemm_128x128_tiles(orc, wq, mode, bits, gs, dt):
+    """The decodes that run 128 x 128 workgroup tiles above 64 rows: 17
+    row blocks of 64 (ragged last 128-row tile) over a ragged last column
+    block, and 4 row blocks with K split (K = 4096, N = 1024: 16 workgroups
+    of 64 x 256).  The oracle computes a seeded sample of columns / all
+    columns."""
+    for K, N, M in ((512, 15520, 1088), (4096, 1024, 250)):
+        L = make(mode, bits, gs, K, N, 9300 + 7 * mode + bits + dt + M)
+        layer = repack_layer(wq, L)
+        x_bits = wl.make_x(M, K, dt, 23 + mode + bits)
+        print(f"[gemm 128x128] mode={mode} bits={bits} gs={gs} dt={dt} K={K} N={N} M={M}", flush=True)
+        y = wq.wq_gemm(bits_to_tensor(x_bits, act_dtype(dt), "cuda"), layer)
+        torch.cuda.synchronize()
+        cols = np.unique(np.concatenate([wl.sample_cols(N, 96, seed=mode + bits), np.arange(N - 16, N)])).astype(np.int32)
+        if N <= 1024:
+            cols = np.arange(N, dtype=np.int32)
+        ok, err, bound = within_tolerance(tensor_f64(y)[:, cols], oracle_y(orc, x_bits, dt, L, cols))
+        assert ok, f"K={K} N={N} M={M}: max error {err:.3e} > bound {bound:.3e}"
+
+
 def test_m_zero_is_a_noop(wq):
     L = make(wl.SYM, 4, 128, 512, 64, 5)
     layer = repack_layer(wq, L)

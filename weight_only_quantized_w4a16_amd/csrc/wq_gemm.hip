@@ -4,16 +4,16 @@
 // the weights on the fly before the multiply, no slowdown with context
 // length).  On gfx950 the product runs on 16x16x32 MFMAs:
 //
-//  * workgroup tile BM x 256 (BM = 128, or 64 for small M), four waves side
-//    by side along N: each wave owns 64 columns for all BM rows, so every
-//    weight fragment is dequantised exactly once per workgroup and reused by
-//    BM / 16 MFMAs;
+//  * workgroup tile BM x BN (128 x 256, 128 x 128 or 64 x 256, by the decode's
+//    register needs and M), four waves side by side along N: each wave owns
+//    BN / 4 columns for all BM rows, so every weight fragment is dequantised
+//    exactly once per workgroup and reused by BM / 16 MFMAs;
 //  * the activation tile (BM rows x 128 k) is staged through LDS by buffer
 //    loads that write LDS directly (no staging registers), double buffered;
 //    16-byte chunks are XOR-swizzled by row -- the swizzle is applied on the
 //    source side, since a wave's load lands contiguously -- so the MFMA A
 //    reads of 16 rows hit 16 different bank groups;
-//  * each wave loads the packed codes of its 64 columns straight from global
+//  * each wave loads the packed codes of its columns straight from global
 //    memory -- the tile layout already is the MFMA B operand, one 128-bit load
 //    per lane per tile -- and dequantises them in registers with the exact
 //    decode (RN(s*(q - z)) or RN(s*T[q]) in the activation dtype), so the
@@ -50,14 +50,13 @@ struct GemmArgs {
 // memory operations are outstanding and leaves the other counters alone.
 constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
-template <int DT, int BITS, int MODE, int GPU, bool EPI_SCALE, int BM>
+template <int DT, int BITS, int MODE, int GPU, bool EPI_SCALE, int BM, int NT>
 __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
-  constexpr int BN = 256;
+  constexpr int BN = 64 * NT;         // NT 16-column tiles per wave, four waves
   constexpr int KT = BITS == 2 ? 256 : 128;
   constexpr int UPT = KT / 128;
   constexpr int WPL = BITS == 3 ? 3 : 4;
   constexpr int MT = BM / 16;         // 16-row subtiles per wave (a wave covers all BM rows)
-  constexpr int NT = 4;               // 16-column tiles per wave (64 columns)
   constexpr int KBPG = 4 / GPU;
   constexpr bool TABLE = MODE == LUT;
   constexpr bool Z16 = MODE == ZERO_F16;
@@ -433,33 +432,56 @@ __global__ __launch_bounds__(256) void ksplit_reduce_kernel(const float* __restr
 
 template <int DT, int BITS, int MODE, int GPU, bool EPI>
 wq_status run_gemm(GemmArgs g, hipStream_t s) {
-  // 128-row tiles unless that leaves fewer than about two workgroups per CU
-  // (a K split always runs 64-row tiles), and only for the decodes whose
-  // 128-row variant fits the 256 registers of a lane without spilling and
-  // keeps two workgroups per CU: symmetric 3- and 4-bit codes (4-bit with at
-  // most two groups per 128 rows), fp16 zero-points with one group per 128
-  // rows, 3-bit integer zero-points with one group per 128 rows, 3-bit tables
-  // (4-bit tables fit too, but their 32 KiB LDS table leaves one workgroup
-  // per CU: 8-12 % slower).  The others spill at 128 rows, up to 2.8x slower
-  // than decoding each weight for half as many rows.  Measured gains of the
-  // 128-row tiles at M = 2048-4096: 7-31 % on fp16 zero-points and 3-bit
-  // tables.
+  // Workgroup tile.  Each wave covers all BM rows of its columns, so a weight
+  // is decoded once per BM rows; the accumulators (BM x 64 / 64 per lane at
+  // four column tiles) and the weight registers must fit 256 per lane for
+  // two workgroups per CU.
+  //  * 128 x 256 (four column tiles per wave) for the decodes that fit it:
+  //    symmetric 3- and 4-bit codes (4-bit with at most two groups per 128
+  //    rows), fp16 zero-points with one group per 128 rows, 3-bit integer
+  //    zero-points with one group per 128 rows, 3-bit tables -- unless that
+  //    leaves fewer than about two workgroups per CU or K is split.  Measured
+  //    gains at M = 2048-4096: 7-31 % on fp16 zero-points and 3-bit tables.
+  //  * 128 x 128 (two column tiles per wave) for the other decodes (more
+  //    groups or zero-point records per tile, 2-bit codes, fine zero-points),
+  //    which spill at 128 x 256 (up to 2.8x slower): half the decode work of
+  //    64 x 256 per output, for as many workgroups, with or without a K
+  //    split.  Measured: 10-40 % faster at M = 80-4096 (the 16384 x 53248
+  //    bf16 packed-zero layer at M = 128: 390 -> 279 us); not taken when the
+  //    rows fill an odd number of 64-row blocks below 7 (M = 192: a padded
+  //    half tile and a third more workgroups, 10 % slower), nor for 4-bit
+  //    tables, whose 32 KiB LDS table leaves one such workgroup per CU (20 %
+  //    slower).  On the first kind 128 x 128 loses 0-11 % to 128 x 256.
+  //  * 64 x 256 otherwise (M <= 64 among them).
+  // The K split (chosen by the host for 64 x 256 workgroups) keeps its slice
+  // count whichever tile runs.
   constexpr bool FIT128 = (MODE == SYM && BITS != 2 && (BITS == 3 || GPU <= 2)) ||
                           (MODE == ZERO_F16 && BITS != 2 && GPU == 1) ||
                           (MODE == ZERO_PACKED && BITS == 3 && GPU == 1) ||
                           (MODE == LUT && BITS == 3);
-  constexpr bool HEAVY = !FIT128;
-  g.ntiles_wg = (g.N + 255) / 256;
-  const int bm =
-      (HEAVY || g.ksplit > 1 || g.M <= 64 || (long)((g.M + 127) / 128) * g.ntiles_wg < 480) ? 64 : 128;
+  constexpr bool NARROW128 = !FIT128 && !(MODE == LUT && BITS == 4);
+  const int blocks64 = (g.M + 63) / 64;
+  int bm = 64, nt = 4;
+  if (NARROW128) {
+    if (g.M > 64 && (blocks64 % 2 == 0 || blocks64 >= 7)) {
+      bm = 128;
+      nt = 2;
+    }
+  } else if (FIT128 && g.ksplit == 1 && g.M > 64 && (long)((g.M + 127) / 128) * ((g.N + 255) / 256) >= 480) {
+    bm = 128;
+  }
+  g.ntiles_wg = (g.N + 64 * nt - 1) / (64 * nt);
   g.mtiles = (g.M + bm - 1) / bm;
   g.ktps = (g.ktiles + g.ksplit - 1) / g.ksplit;
   const int grid = g.mtiles * g.ntiles_wg * g.ksplit;
   if (bm == 64) {
-    hipLaunchKernelGGL((gemm_kernel<DT, BITS, MODE, GPU, EPI, 64>), dim3(grid), dim3(256), 0, s, g);
+    hipLaunchKernelGGL((gemm_kernel<DT, BITS, MODE, GPU, EPI, 64, 4>), dim3(grid), dim3(256), 0, s, g);
+  } else if (nt == 2) {
+    if constexpr (NARROW128)
+      hipLaunchKernelGGL((gemm_kernel<DT, BITS, MODE, GPU, EPI, 128, 2>), dim3(grid), dim3(256), 0, s, g);
   } else {
-    if constexpr (!HEAVY)
-      hipLaunchKernelGGL((gemm_kernel<DT, BITS, MODE, GPU, EPI, 128>), dim3(grid), dim3(256), 0, s, g);
+    if constexpr (FIT128)
+      hipLaunchKernelGGL((gemm_kernel<DT, BITS, MODE, GPU, EPI, 128, 4>), dim3(grid), dim3(256), 0, s, g);
   }
   if (g.ksplit > 1) {
     const size_t quads = (size_t)g.M * (g.swiglu ? g.N / 2 : g.N) / 4;
