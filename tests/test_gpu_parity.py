@@ -141,7 +141,8 @@ def test_gemm_128_row_tiles(orc, wq, mode, bits, gs, dt):
 
 NARROW_TILE_CASES = [(wl.SYM, 4, 32), (wl.SYM, 2, 128), (wl.ZERO_F16, 4, 64), (wl.ZERO_F16, 2, 256),
                      (wl.ZERO_PACKED, 4, 128), (wl.ZERO_PACKED, 4, 32), (wl.ZERO_PACKED, 3, 64),
-                     (wl.ZERO_PACKED, 2, 256), (wl.LUT, 2, 64), (wl.ZERO_F16_G8, 4, -1), (wl.ZERO_F16_G32, 3, 128)]
+                     (wl.ZERO_PACKED, 2, 256), (wl.LUT, 2, 64), (wl.LUT, 4, 64), (wl.LUT, 4, -1),
+                     (wl.ZERO_F16_G8, 4, -1), (wl.ZERO_F16_G32, 3, 128)]
 
 
 @pytest.mark.parametrize("mode,bits,gs", NARROW_TILE_CASES)

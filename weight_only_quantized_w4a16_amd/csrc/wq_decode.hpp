@@ -273,9 +273,10 @@ __device__ inline uint32_t fine_zero_bits(const uint32_t* zr, int kbu) {
 
 // ---------------------------------------------------------------------------
 // Table decode: B operand from an LDS pair table.  tab points at the table's
-// column for this lane (base + (lane % 32)); entry idx sits at tab[idx * 32].
+// column for this lane (base + lane % COPIES); entry idx sits at
+// tab[idx * COPIES].
 // ---------------------------------------------------------------------------
-template <int BITS, int KB>
+template <int BITS, int KB, int COPIES = 32>
 __device__ inline u32x4 table_frag(const uint32_t* w, const uint32_t* tab) {
   u32x4 r;
 #pragma unroll
@@ -297,20 +298,20 @@ __device__ inline u32x4 table_frag(const uint32_t* w, const uint32_t* tab) {
         case 14: idx = pair6<14>(w); break; default: idx = pair6<15>(w); break;
       }
     }
-    r[q] = tab[idx * 32];
+    r[q] = tab[idx * COPIES];
   }
   return r;
 }
 
 // Fill an LDS pair table: entry idx = value[lo] | value[hi] << 16 with
-// lo = idx & (2^BITS - 1), hi = idx >> BITS, replicated over 32 columns.
+// lo = idx & (2^BITS - 1), hi = idx >> BITS, replicated over COPIES columns.
 // AS_BF16: store RN_bf16(T) instead of the fp16 T.
-template <int BITS, bool AS_BF16>
+template <int BITS, bool AS_BF16, int COPIES = 32>
 __device__ inline void fill_pair_table(uint32_t* table, const uint16_t* lut, int tid, int nthreads) {
   constexpr int n = 1 << (2 * BITS);
   constexpr int mask = (1 << BITS) - 1;
-  for (int i = tid; i < n * 32; i += nthreads) {
-    const int idx = i >> 5;
+  for (int i = tid; i < n * COPIES; i += nthreads) {
+    const int idx = i / COPIES;
     uint16_t lo = lut[idx & mask], hi = lut[idx >> BITS];
     if (AS_BF16) {
       lo = f32_to_bf16(f16_to_f32(lo));
@@ -348,7 +349,7 @@ struct ExactParams {
 
 // Exact dequantised B operand for k-block KB: RN_dt(s*(q - z)) or RN_dt(s*T[q]).
 // tab: LDS fp16 pair table column for this lane (table mode only).
-template <int BITS, int DT, int MODE, int KB>
+template <int BITS, int DT, int MODE, int KB, int COPIES = 32>
 __device__ inline u32x4 exact_frag(const uint32_t* w, const ExactParams& p, const uint32_t* tab,
                                    const DecodeConsts& k) {
   u32x4 r;
@@ -358,13 +359,13 @@ __device__ inline u32x4 exact_frag(const uint32_t* w, const ExactParams& p, cons
 #pragma unroll
     for (int q = 0; q < 4; ++q) r[q] = as_u32(as_h2(o[q]) * p.s_h);
   } else if constexpr (MODE == LUT && DT == F16) {
-    const u32x4 t = table_frag<BITS, KB>(w, tab);
+    const u32x4 t = table_frag<BITS, KB, COPIES>(w, tab);
 #pragma unroll
     for (int q = 0; q < 4; ++q) r[q] = as_u32(as_h2(t[q]) * p.s_h);
   } else if constexpr (MODE == LUT) {
     // fp16 table values widened inside v_fma_mix: s * T exact in fp32 (adding
     // -0 keeps the product's sign), one rounding to bf16
-    const u32x4 t = table_frag<BITS, KB>(w, tab);
+    const u32x4 t = table_frag<BITS, KB, COPIES>(w, tab);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const h2 v = as_h2(t[q]);
@@ -412,7 +413,7 @@ __device__ inline u32x4 exact_frag(const uint32_t* w, const ExactParams& p, cons
 //     11 significant bits) and then scaled: RN(s * RN(q - z)), at most one
 //     extra rounding away from RN(s * (q - z));
 // every other case takes the exact decode above.
-template <int BITS, int DT, int MODE, int KB>
+template <int BITS, int DT, int MODE, int KB, int COPIES = 32>
 __device__ inline u32x4 product_frag(const uint32_t* w, const ExactParams& p, const uint32_t* tab,
                                      const DecodeConsts& k) {
   if constexpr (DT == F16 && (MODE == ZERO_F16 || MODE == ZFINE || MODE == ZERO_PACKED)) {
@@ -426,7 +427,7 @@ __device__ inline u32x4 product_frag(const uint32_t* w, const ExactParams& p, co
     }
     return r;
   } else {
-    return exact_frag<BITS, DT, MODE, KB>(w, p, tab, k);
+    return exact_frag<BITS, DT, MODE, KB, COPIES>(w, p, tab, k);
   }
 }
 

@@ -67,7 +67,11 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
   constexpr int ZW = MODE == ZERO_PACKED ? GPU : FINE ? 2 : 1;
   constexpr int AW = BM / 16;         // 1-KiB activation loads per wave per unit
 
-  __shared__ uint32_t table[TABLE ? (32 << (2 * BITS)) : 1];
+  // Table columns: 32 (one per lane of a half-wave), 16 for 4-bit tables in
+  // 128 x 128 tiles, whose 80 KiB of LDS (16 KiB table + two 32 KiB stages)
+  // then leave room for two workgroups per CU.
+  constexpr int COPIES = (TABLE && BITS == 4 && NT == 2) ? 16 : 32;
+  __shared__ uint32_t table[TABLE ? (COPIES << (2 * BITS)) : 1];
   // Two stages of the BM x 128 activation tile, 16-byte chunks, row r at
   // chunk (c ^ (r % 16)).  Separate arrays so each stage's reads and loads are
   // distinct objects.
@@ -99,8 +103,8 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
   const uint32_t zf_rec = 8u * hcs;
   const uint32_t zf_lane = (uint32_t)c * zf_rec + 8u * ((h * hcs) >> 2);
 
-  if constexpr (TABLE) fill_pair_table<BITS, false>(table, a.lut, tid, 256);
-  const uint32_t* tab = table + (lane & 31);
+  if constexpr (TABLE) fill_pair_table<BITS, false, COPIES>(table, a.lut, tid, 256);
+  const uint32_t* tab = table + (lane % COPIES);
   const DecodeConsts dk = make_decode_consts<DT>();
 
   // ---- activations: wave issues AW LDS-destination loads of 1 KiB per unit.
@@ -234,9 +238,9 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
             const float zk = f16_to_f32((uint16_t)fine_zero_bits(cz[t], kbu));
             pk.sz = pk.s * zk;
             pk.nz_h = h2s(-zk);
-            bf[t] = product_frag<BITS, DT, MODE, kb>(cw[t], pk, tab, dk);
+            bf[t] = product_frag<BITS, DT, MODE, kb, COPIES>(cw[t], pk, tab, dk);
           } else {
-            bf[t] = product_frag<BITS, DT, MODE, kb>(cw[t], prm[t], tab, dk);
+            bf[t] = product_frag<BITS, DT, MODE, kb, COPIES>(cw[t], prm[t], tab, dk);
           }
         }
       }
@@ -447,11 +451,11 @@ wq_status run_gemm(GemmArgs g, hipStream_t s) {
   //    which spill at 128 x 256 (up to 2.8x slower): half the decode work of
   //    64 x 256 per output, for as many workgroups, with or without a K
   //    split.  Measured: 10-40 % faster at M = 80-4096 (the 16384 x 53248
-  //    bf16 packed-zero layer at M = 128: 390 -> 279 us); not taken when the
-  //    rows fill an odd number of 64-row blocks below 7 (M = 192: a padded
-  //    half tile and a third more workgroups, 10 % slower), nor for 4-bit
-  //    tables, whose 32 KiB LDS table leaves one such workgroup per CU (20 %
-  //    slower).  On the first kind 128 x 128 loses 0-11 % to 128 x 256.
+  //    bf16 packed-zero layer at M = 128: 390 -> 279 us; 4-bit tables, with
+  //    their table in 16 columns, 10-25 %); not taken when the rows fill an
+  //    odd number of 64-row blocks below 7 (M = 192: a padded half tile and a
+  //    third more workgroups, 10 % slower).  On the first kind 128 x 128
+  //    loses 0-11 % to 128 x 256.
   //  * 64 x 256 otherwise (M <= 64 among them).
   // The K split (chosen by the host for 64 x 256 workgroups) keeps its slice
   // count whichever tile runs.
@@ -459,7 +463,7 @@ wq_status run_gemm(GemmArgs g, hipStream_t s) {
                           (MODE == ZERO_F16 && BITS != 2 && GPU == 1) ||
                           (MODE == ZERO_PACKED && BITS == 3 && GPU == 1) ||
                           (MODE == LUT && BITS == 3);
-  constexpr bool NARROW128 = !FIT128 && !(MODE == LUT && BITS == 4);
+  constexpr bool NARROW128 = !FIT128;
   const int blocks64 = (g.M + 63) / 64;
   int bm = 64, nt = 4;
   if (NARROW128) {
