@@ -242,6 +242,16 @@ __device__ inline u32x4 biased_frag(const uint32_t* w, const DecodeConsts& k) {
   return biased_frag<BITS, KB>(w, k, k.magic);
 }
 
+// 4-bit codes as fp16 pairs with one shift per word: pairs 0 and 2 are
+// 1024 + q (nibbles at bits 0-3 / 16-19 of x and of x >> 8), pairs 1 and 3
+// are 1024 + 16 q (nibbles at bits 4-7 / 20-23 masked in place), both exact.
+template <int KB>
+__device__ inline u32x4 split4_frag(const uint32_t* w, const DecodeConsts& k) {
+  const uint32_t x = w[KB], x8 = x >> 8;
+  return u32x4{(x & k.m4lo) | k.magic_h, (x & k.m4hi) | k.magic_h, (x8 & k.m4lo) | k.magic_h,
+               (x8 & k.m4hi) | k.magic_h};
+}
+
 // Fine zero-points, scale applied later: B operand RN_dt(q - z) for k-block KB,
 // whose eight rows share one zero-point z (fp16 bits zbits).
 //   fp16: (1024 + q) - 1024 is exact, one packed add of -z rounds once;
@@ -378,9 +388,22 @@ __device__ inline u32x4 exact_frag(const uint32_t* w, const ExactParams& p, cons
     //   fp16 zero-points: s * (1024 + q) - 1024 s = s * q exactly, then
     //     minus s * z (exact) rounds once to the exact s * (q - z);
     // then one rounding to bf16.
-    const u32x4 o = biased_frag<BITS, KB>(w, k, k.magic_h);
     constexpr bool INT_Z = MODE == SYM || MODE == ZERO_PACKED;
     const float c = INT_Z ? -__builtin_fmaf(1024.0f, p.s, p.sz) : -1024.0f * p.s;
+    if constexpr (BITS == 4 && INT_Z) {
+      // odd pairs hold 1024 + 16 q: (1024 + 16 q) * (s / 16) - s * (64 + z),
+      // every term exact as above
+      const u32x4 o = split4_frag<KB>(w, k);
+      const float s16 = p.s * 0.0625f, c16 = -__builtin_fmaf(64.0f, p.s, p.sz);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const h2 v = as_h2(o[q]);
+        const float sq = (q & 1) ? s16 : p.s, cq = (q & 1) ? c16 : c;
+        r[q] = pack2<DT>(__builtin_fmaf((float)v[0], sq, cq), __builtin_fmaf((float)v[1], sq, cq));
+      }
+      return r;
+    }
+    const u32x4 o = biased_frag<BITS, KB>(w, k, k.magic_h);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const h2 v = as_h2(o[q]);
