@@ -145,15 +145,17 @@ NARROW_TILE_CASES = [(wl.SYM, 4, 32), (wl.SYM, 2, 128), (wl.ZERO_F16, 4, 64), (w
                      (wl.ZERO_F16_G8, 4, -1), (wl.ZERO_F16_G32, 3, 128)]
 
 
-@pytest.mark.parametrize("mode,bits,gs", NARROW_TILE_CASES)
+@pytest.mark.parametrize("mode,bits,gs,shapes", [c + (((512, 15520, 1088), (4096, 1024, 250)),) for c in NARROW_TILE_CASES]
+                         + [c + (((512, 2080, 1088), (4096, 1024, 250)),) for c in TILE128_CASES])
 @pytest.mark.parametrize("dt", [wl.F16, wl.BF16])
-def test_gemm_128x128_tiles(orc, wq, mode, bits, gs, dt):
-    """The decodes that run 128 x 128 workgroup tiles above 64 rows: 17
-    row blocks of 64 (ragged last 128-row tile) over a ragged last column
-    block, and 4 row blocks with K split (K = 4096, N = 1024: 16 workgroups
-    of 64 x 256).  The oracle computes a seeded sample of columns / all
-    columns."""
-    for K, N, M in ((512, 15520, 1088), (4096, 1024, 250)):
+def test_gemm_128x128_tiles(orc, wq, mode, bits, gs, shapes, dt):
+    """128 x 128 workgroup tiles above 64 rows: 17 row blocks of 64 (ragged
+    last 128-row tile) over a ragged last column block, and 4 row blocks with
+    K split (K = 4096, N = 1024: 16 workgroups of 64 x 256).  Decodes that
+    fit 128 x 256 tiles take 128 x 128 where 128 x 256 would leave too few
+    workgroups (N = 2080) or K is split.  The oracle computes a seeded
+    sample of columns / all columns."""
+    for K, N, M in shapes:
         L = make(mode, bits, gs, K, N, 9300 + 7 * mode + bits + dt + M)
         layer = repack_layer(wq, L)
         x_bits = wl.make_x(M, K, dt, 23 + mode + bits)

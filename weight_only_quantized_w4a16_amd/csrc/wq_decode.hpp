@@ -359,7 +359,7 @@ struct ExactParams {
 
 // Exact dequantised B operand for k-block KB: RN_dt(s*(q - z)) or RN_dt(s*T[q]).
 // tab: LDS fp16 pair table column for this lane (table mode only).
-template <int BITS, int DT, int MODE, int KB, int COPIES = 32>
+template <int BITS, int DT, int MODE, int KB, int COPIES = 32, bool SPLIT4 = true>
 __device__ inline u32x4 exact_frag(const uint32_t* w, const ExactParams& p, const uint32_t* tab,
                                    const DecodeConsts& k) {
   u32x4 r;
@@ -390,7 +390,7 @@ __device__ inline u32x4 exact_frag(const uint32_t* w, const ExactParams& p, cons
     // then one rounding to bf16.
     constexpr bool INT_Z = MODE == SYM || MODE == ZERO_PACKED;
     const float c = INT_Z ? -__builtin_fmaf(1024.0f, p.s, p.sz) : -1024.0f * p.s;
-    if constexpr (BITS == 4 && INT_Z) {
+    if constexpr (SPLIT4 && BITS == 4 && INT_Z) {
       // odd pairs hold 1024 + 16 q: (1024 + 16 q) * (s / 16) - s * (64 + z),
       // every term exact as above
       const u32x4 o = split4_frag<KB>(w, k);
@@ -436,7 +436,7 @@ __device__ inline u32x4 exact_frag(const uint32_t* w, const ExactParams& p, cons
 //     11 significant bits) and then scaled: RN(s * RN(q - z)), at most one
 //     extra rounding away from RN(s * (q - z));
 // every other case takes the exact decode above.
-template <int BITS, int DT, int MODE, int KB, int COPIES = 32>
+template <int BITS, int DT, int MODE, int KB, int COPIES = 32, bool SPLIT4 = true>
 __device__ inline u32x4 product_frag(const uint32_t* w, const ExactParams& p, const uint32_t* tab,
                                      const DecodeConsts& k) {
   if constexpr (DT == F16 && (MODE == ZERO_F16 || MODE == ZFINE || MODE == ZERO_PACKED)) {
@@ -450,7 +450,7 @@ __device__ inline u32x4 product_frag(const uint32_t* w, const ExactParams& p, co
     }
     return r;
   } else {
-    return exact_frag<BITS, DT, MODE, KB, COPIES>(w, p, tab, k);
+    return exact_frag<BITS, DT, MODE, KB, COPIES, SPLIT4>(w, p, tab, k);
   }
 }
 

@@ -71,6 +71,9 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
   // 128 x 128 tiles, whose 80 KiB of LDS (16 KiB table + two 32 KiB stages)
   // then leave room for two workgroups per CU.
   constexpr int COPIES = (TABLE && BITS == 4 && NT == 2) ? 16 : 32;
+  // one-shift nibble decode (bf16) except in 128 x 256 tiles, where its two
+  // extra registers per column tile would spill
+  constexpr bool SPLIT4 = !(BM == 128 && NT == 4);
   __shared__ uint32_t table[TABLE ? (COPIES << (2 * BITS)) : 1];
   // Two stages of the BM x 128 activation tile, 16-byte chunks, row r at
   // chunk (c ^ (r % 16)).  Separate arrays so each stage's reads and loads are
@@ -238,9 +241,9 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
             const float zk = f16_to_f32((uint16_t)fine_zero_bits(cz[t], kbu));
             pk.sz = pk.s * zk;
             pk.nz_h = h2s(-zk);
-            bf[t] = product_frag<BITS, DT, MODE, kb, COPIES>(cw[t], pk, tab, dk);
+            bf[t] = product_frag<BITS, DT, MODE, kb, COPIES, SPLIT4>(cw[t], pk, tab, dk);
           } else {
-            bf[t] = product_frag<BITS, DT, MODE, kb, COPIES>(cw[t], prm[t], tab, dk);
+            bf[t] = product_frag<BITS, DT, MODE, kb, COPIES, SPLIT4>(cw[t], prm[t], tab, dk);
           }
         }
       }
@@ -440,22 +443,26 @@ wq_status run_gemm(GemmArgs g, hipStream_t s) {
   // is decoded once per BM rows; the accumulators (BM x 64 / 64 per lane at
   // four column tiles) and the weight registers must fit 256 per lane for
   // two workgroups per CU.
-  //  * 128 x 256 (four column tiles per wave) for the decodes that fit it:
+  //  * 128 x 256 (four column tiles per wave) for the decodes that fit it --
   //    symmetric 3- and 4-bit codes (4-bit with at most two groups per 128
   //    rows), fp16 zero-points with one group per 128 rows, 3-bit integer
-  //    zero-points with one group per 128 rows, 3-bit tables -- unless that
-  //    leaves fewer than about two workgroups per CU or K is split.  Measured
-  //    gains at M = 2048-4096: 7-31 % on fp16 zero-points and 3-bit tables.
-  //  * 128 x 128 (two column tiles per wave) for the other decodes (more
-  //    groups or zero-point records per tile, 2-bit codes, fine zero-points),
-  //    which spill at 128 x 256 (up to 2.8x slower): half the decode work of
-  //    64 x 256 per output, for as many workgroups, with or without a K
-  //    split.  Measured: 10-40 % faster at M = 80-4096 (the 16384 x 53248
-  //    bf16 packed-zero layer at M = 128: 390 -> 279 us; 4-bit tables, with
-  //    their table in 16 columns, 10-25 %); not taken when the rows fill an
-  //    odd number of 64-row blocks below 7 (M = 192: a padded half tile and a
-  //    third more workgroups, 10 % slower).  On the first kind 128 x 128
-  //    loses 0-11 % to 128 x 256.
+  //    zero-points with one group per 128 rows, 3-bit tables -- when K is not
+  //    split and the grid holds at least about two workgroups per CU.
+  //    Measured gains at M = 2048-4096: 7-31 % on fp16 zero-points and 3-bit
+  //    tables; 128 x 128 loses 0-11 % to it there.
+  //  * otherwise above M = 64, 128 x 128 (two column tiles per wave): half
+  //    the decode work of 64 x 256 per output for as many workgroups, with or
+  //    without a K split.  The decodes that spill at 128 x 256 (more groups or
+  //    zero-point records per tile, 2-bit codes, fine zero-points, 4-bit
+  //    tables) always take it there.  Measured 5-40 % faster than 64 x 256
+  //    at M = 80-4096 (the 16384 x 53248 bf16 packed-zero layer at M = 128:
+  //    390 -> 279 us; 4096-column layers at M = 2048: 7-23 %; 4-bit tables,
+  //    with their table in 16 columns, 10-25 %).  Not taken when the rows
+  //    fill an odd number of 64-row blocks below 7 (M = 192: a padded half
+  //    tile and a third more workgroups, 10 % slower), nor for the cheapest
+  //    decode (fp16 symmetric codes, scale in the epilogue) when 64 x 256
+  //    tiles fill two workgroups per CU: there the doubled LDS reads of the
+  //    activations cost more than the decode saves (3-8 % slower).
   //  * 64 x 256 otherwise (M <= 64 among them).
   // The K split (chosen by the host for 64 x 256 workgroups) keeps its slice
   // count whichever tile runs.
@@ -463,16 +470,14 @@ wq_status run_gemm(GemmArgs g, hipStream_t s) {
                           (MODE == ZERO_F16 && BITS != 2 && GPU == 1) ||
                           (MODE == ZERO_PACKED && BITS == 3 && GPU == 1) ||
                           (MODE == LUT && BITS == 3);
-  constexpr bool NARROW128 = !FIT128;
   const int blocks64 = (g.M + 63) / 64;
   int bm = 64, nt = 4;
-  if (NARROW128) {
-    if (g.M > 64 && (blocks64 % 2 == 0 || blocks64 >= 7)) {
-      bm = 128;
-      nt = 2;
-    }
-  } else if (FIT128 && g.ksplit == 1 && g.M > 64 && (long)((g.M + 127) / 128) * ((g.N + 255) / 256) >= 480) {
+  if (FIT128 && g.ksplit == 1 && g.M > 64 && (long)((g.M + 127) / 128) * ((g.N + 255) / 256) >= 480) {
     bm = 128;
+  } else if (g.M > 64 && (blocks64 % 2 == 0 || blocks64 >= 7) &&
+             !(EPI && (long)blocks64 * ((g.N + 255) / 256) * g.ksplit >= 512)) {
+    bm = 128;
+    nt = 2;
   }
   g.ntiles_wg = (g.N + 64 * nt - 1) / (64 * nt);
   g.mtiles = (g.M + bm - 1) / bm;
@@ -481,8 +486,7 @@ wq_status run_gemm(GemmArgs g, hipStream_t s) {
   if (bm == 64) {
     hipLaunchKernelGGL((gemm_kernel<DT, BITS, MODE, GPU, EPI, 64, 4>), dim3(grid), dim3(256), 0, s, g);
   } else if (nt == 2) {
-    if constexpr (NARROW128)
-      hipLaunchKernelGGL((gemm_kernel<DT, BITS, MODE, GPU, EPI, 128, 2>), dim3(grid), dim3(256), 0, s, g);
+    hipLaunchKernelGGL((gemm_kernel<DT, BITS, MODE, GPU, EPI, 128, 2>), dim3(grid), dim3(256), 0, s, g);
   } else {
     if constexpr (FIT128)
       hipLaunchKernelGGL((gemm_kernel<DT, BITS, MODE, GPU, EPI, 128, 4>), dim3(grid), dim3(256), 0, s, g);
