@@ -461,8 +461,9 @@ wq_status run_gemm(GemmArgs g, hipStream_t s) {
   //    fill an odd number of 64-row blocks below 7 (M = 192: a padded half
   //    tile and a third more workgroups, 10 % slower), nor for the cheapest
   //    decode (fp16 symmetric codes, scale in the epilogue) when 64 x 256
-  //    tiles fill two workgroups per CU: there the doubled LDS reads of the
-  //    activations cost more than the decode saves (3-8 % slower).
+  //    tiles more than fill two workgroups per CU: there the doubled LDS
+  //    reads of the activations cost more than the decode saves (3-8 %
+  //    slower at 768 and more workgroups; 7 % faster at 512).
   //  * 64 x 256 otherwise (M <= 64 among them).
   // The K split (chosen by the host for 64 x 256 workgroups) keeps its slice
   // count whichever tile runs.
@@ -475,7 +476,7 @@ wq_status run_gemm(GemmArgs g, hipStream_t s) {
   if (FIT128 && g.ksplit == 1 && g.M > 64 && (long)((g.M + 127) / 128) * ((g.N + 255) / 256) >= 480) {
     bm = 128;
   } else if (g.M > 64 && (blocks64 % 2 == 0 || blocks64 >= 7) &&
-             !(EPI && (long)blocks64 * ((g.N + 255) / 256) * g.ksplit >= 512)) {
+             !(EPI && (long)blocks64 * ((g.N + 255) / 256) * g.ksplit > 512)) {
     bm = 128;
     nt = 2;
   }
