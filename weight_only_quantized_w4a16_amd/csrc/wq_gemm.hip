@@ -83,7 +83,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // -> 64-column slice
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // -> its BN / 4 columns
   const int c = lane & 15, h = lane >> 4;
 
   // Tile order: M fastest.  Workgroups are dispatched to the 8 XCDs
@@ -186,7 +186,6 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[i][t] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // One 128-row unit of K from stage `As`: 4 k-blocks of MT x NT MFMAs.
   // A fragment (activation rows 16 i .. 16 i + 15, k-block kbu) from stage As.
   auto a_frag = [&](const u32x4* As, int kbu, int i) {
     const int r = 16 * i + c;
@@ -195,9 +194,9 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
   // One 128-row unit of K from stage `As`: 4 k-blocks of MT x NT MFMAs, taken
   // as pairs of row subtiles.  With 128-row tiles the A fragments of the next
   // pair are read from LDS before the MFMAs of the current pair are issued, so
-  // each read has a whole pair of MFMAs (8 x NT) to complete; with 64-row
-  // tiles the extra registers would cost a wave per SIMD, so the reads stay
-  // next to their MFMAs.
+  // each read has the pair's 2 NT MFMAs to complete; with 64-row tiles the
+  // extra registers would cost a wave per SIMD, so the reads stay next to
+  // their MFMAs.
   constexpr bool LOOKAHEAD = BM == 128;
   auto compute_unit = [&](const u32x4* As, const uint32_t (&cw)[NT][WPL], const uint32_t (&cs)[NT][SW],
                           const uint32_t (&cz)[NT][ZW], auto uc) {
