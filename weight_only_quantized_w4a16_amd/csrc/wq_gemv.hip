@@ -14,11 +14,13 @@
 //  * Codes become MFMA B operands in registers (offset or table decode);
 //    16x16x32 MFMAs do the multiply-accumulate, which leaves the vector ALUs
 //    to the decode.
-//  * Scales are applied after the MFMA, per 128-row unit of K, in fp32:
-//    sum_k x*s*(q - z) = s*(sum_k x*B - c*sum_k x) with B = bias + q the
-//    decoded operand and c = bias + z; sum_k x comes from one more MFMA
-//    against a B of ones.  No per-element float work at all: the products
-//    x*B are exact in fp32 and the bias cancels in the correction.
+//  * With fp16 activations scales are applied after the MFMA, per 128-row
+//    unit of K, in fp32: sum_k x*s*(q - z) = s*(sum_k x*B - c*sum_k x) with
+//    B = bias + q the decoded operand and c = bias + z; sum_k x comes from one
+//    more MFMA against a B of ones.  No per-element float work at all: the
+//    products x*B are exact in fp32 and the bias cancels in the correction.
+//    With bf16 activations the operand is the dequantised weight itself
+//    (exact product, one rounding to bf16), as in the large-M product.
 //  * M <= 4 packs (row m, k-block kb) into MFMA row 4m + kb, so one 128-bit
 //    activation load feeds the 4 k-blocks of a unit; larger M uses one MFMA
 //    row per activation row (blocks of 16 rows, two for M > 16), loading
@@ -47,21 +49,26 @@ struct GemvArgs {
   int zg;                 // rows per fine zero-point group (8, 16, 32; fine mode only)
 };
 
-// Decode k-block KB of a tile into a B operand (fine mode only: zbits is the
-// k-block's zero-point, s its scale).  Fine zero-points with fp16 activations
-// give RN(q - z) (11 bits, the scale comes after the MFMA); with bf16
-// activations RN(q - z) would keep only 8 bits, so the weight is the
-// dequantised RN(s * (q - z)) itself and no scale follows.
+// Decode k-block KB of a tile into a B operand.  fp16 activations: the
+// biased code bias + q (scale and zero-point follow the MFMA), the table
+// value T[q], or, for fine zero-points, RN(q - z) with zbits the k-block's
+// zero-point (11 bits, the scale follows the MFMA).  bf16 activations: the
+// dequantised weight RN_bf16(s * (q - z)) or RN_bf16(s * T[q]) itself (z the
+// group's zero-point, or the fine one in zbits) and no scale follows: a bf16
+// operand keeps only 8 bits, so applying the scale after the MFMA would
+// multiply other weights than the rounded ones the product is defined on --
+// one further bf16 rounding per weight, which with the bf16 rounding of the
+// output measured outside the tolerance on a 2048-row layer.
 template <int BITS, int DT, int MODE, int KB>
 __device__ inline u32x4 decode_frag(const uint32_t* w, const uint32_t* tab, const DecodeConsts& k, uint32_t zbits,
-                                    float s) {
-  if constexpr (MODE == LUT) {
-    return table_frag<BITS, KB>(w, tab);
-  } else if constexpr (MODE == ZFINE && DT == BF16) {
+                                    float s, float z) {
+  if constexpr (DT == BF16) {
     ExactParams p;
     p.s = s;
-    p.sz = s * f16_to_f32((uint16_t)zbits);
+    p.sz = MODE == LUT ? 0.0f : s * (MODE == ZFINE ? f16_to_f32((uint16_t)zbits) : z);
     return exact_frag<BITS, DT, MODE, KB>(w, p, tab, k);
+  } else if constexpr (MODE == LUT) {
+    return table_frag<BITS, KB>(w, tab);
   } else if constexpr (MODE == ZFINE) {
     return fine_frag<BITS, DT, KB>(w, zbits, k);
   } else {
@@ -113,8 +120,8 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU, MR>() ? 512 : 1024)
   constexpr int REC = (Z16 ? 4 : 2) * GPU;      // scale record bytes per column
   constexpr int SW = REC < 4 ? 1 : REC / 4;     // words per scale record
   constexpr int ZREC = 4 * GPU;                 // packed-zero record bytes per column half
-  constexpr bool XS = MODE != LUT && !FINE;     // shared zero-points: remove bias + z via row sums
-  constexpr bool SCALED = FINE && DT == BF16;   // decoded weights already carry the scale
+  constexpr bool SCALED = DT == BF16;          // decoded weights already carry the scale
+  constexpr bool XS = !SCALED && MODE != LUT && !FINE;  // shared zero-points: remove bias + z via row sums
   constexpr int ZW = FINE ? 2 : (HAS_Z && !Z16 ? GPU : 1);  // words of a zero record
   constexpr int NRED = PACKED ? 1 : 4;          // reduced values per lane per column tile
 
@@ -240,7 +247,7 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU, MR>() ? 512 : 1024)
   }
 
   if constexpr (TABLE) {
-    fill_pair_table<BITS, DT == BF16>(table, a.lut, threadIdx.x, a.waves * 64);
+    fill_pair_table<BITS, false>(table, a.lut, threadIdx.x, a.waves * 64);  // fp16 values
     __syncthreads();
   }
   const uint32_t* tab = table + (lane & 31);
@@ -274,7 +281,8 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU, MR>() ? 512 : 1024)
           for (int t = 0; t < TN; ++t) {
             const u32x4 b = decode_frag<BITS, DT, MODE, 4 * u + kb>(
                 f.w[t], tab, dk, FINE ? fine_zero_bits(f.z[t][u], kb) : 0u,
-                SCALED ? rec_scale<Z16>(f.s[t][u], kb / KBPG) : 0.0f);
+                SCALED ? rec_scale<Z16>(f.s[t][u], kb / KBPG) : 0.0f,
+                SCALED && !TABLE && !FINE ? zero_of(f, t, u, kb / KBPG) : 0.0f);
             acc[t][kb] = mfma16<DT>(f.xa[0][u], b, zero4);
           }
         });
@@ -324,7 +332,8 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU, MR>() ? 512 : 1024)
             for (int t = 0; t < TN; ++t) {
               const u32x4 b = decode_frag<BITS, DT, MODE, kb>(
                   f.w[t], tab, dk, FINE ? fine_zero_bits(f.z[t][u], kb - 4 * u) : 0u,
-                  SCALED ? rec_scale<Z16>(f.s[t][u], gi) : 0.0f);
+                  SCALED ? rec_scale<Z16>(f.s[t][u], gi) : 0.0f,
+                  SCALED && !TABLE && !FINE ? zero_of(f, t, u, gi) : 0.0f);
 #pragma unroll
               for (int r = 0; r < MR; ++r) acc[r][t] = mfma16<DT>(xf[r][kb - 4 * u], b, acc[r][t]);
             }
