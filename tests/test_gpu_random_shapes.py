@@ -54,7 +54,9 @@ def draw(seed):
         return dict(bits=bits, mode=mode, dt=dt, gs=gs, K=K, N=N, M=M, act_order=act_order)
 
 
-@pytest.mark.parametrize("seed", range(150))
+# seed 388 (bf16, 4-bit symmetric, group -1, K = 2048, N = 688, M = 3) exceeded
+# the tolerance when the decode-sized product multiplied unrounded bf16 weights
+@pytest.mark.parametrize("seed", list(range(150)) + [388])
 def test_random_problem(orc, wq, seed):
     p = draw(seed)
     print(f"[random] seed={seed} {p}", flush=True)
