@@ -7,17 +7,20 @@
 //  * offset decode (uniform modes): OR-ing a code into the mantissa of a float
 //    whose exponent makes the unit in the last place 1 yields (bias + q)
 //    exactly.  The biased form keeps that value (bias 1024 for fp16, 0x6400;
-//    128 for bf16, 0x4300) and the decode-sized product removes bias + z
-//    after the MFMA with the row sums of x.  The offset form (fp16) removes the
-//    bias with one packed fp16 add or fma, giving q - 2^(bits-1) exactly; the
-//    fma may also scale a field sitting 4^i higher by 4^-i, which saves shifts.
+//    128 for bf16, 0x4300) and the decode-sized product with fp16 activations
+//    removes bias + z after the MFMA with the row sums of x.  The offset form
+//    (fp16) removes the bias with one packed fp16 add or fma, giving
+//    q - 2^(bits-1) exactly; the fma may also scale a field sitting 4^i
+//    higher by 4^-i, which saves shifts.
 //  * table decode: two codes form an index into an LDS table of value pairs
 //    (FLUTE page, "How It Works": value = table entry times scale).  The
-//    table is replicated 32 times so that lane l always reads bank l%32.
-//  * exact decode (the large-M product and the debug dump): the dequantised
-//    weight RN(s*(q - z)) or RN(s*T[q]) in the activation dtype, one rounding
-//    of a value that is exact in fp32 (s has 11 significant bits, q - z at most
-//    13 for fp16 zero-points in the ranges used, T[q] 11).
+//    table is replicated 32 times so that lane l always reads bank l%32 (16
+//    times where LDS is short).
+//  * exact decode (the large-M product, the debug dump, and the decode-sized
+//    product with bf16 activations): the dequantised weight RN(s*(q - z)) or
+//    RN(s*T[q]) in the activation dtype, one rounding of a value that is
+//    exact in fp32 (s has 11 significant bits, q - z at most 13 for fp16
+//    zero-points in the ranges used, T[q] 11).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
