@@ -11,7 +11,7 @@
 //    loads, 1 KiB per wave per tile.  Loads past the range are issued with an
 //    out-of-range offset instead of a branch, so the code stays straight-line
 //    and every wait on the memory counter is exact.
-//  * Codes become MFMA B operands in registers (offset or table decode);
+//  * Codes become MFMA B operands in registers (offset, table or exact decode);
 //    16x16x32 MFMAs do the multiply-accumulate, which leaves the vector ALUs
 //    to the decode.
 //  * With fp16 activations scales are applied after the MFMA, per 128-row
@@ -115,7 +115,7 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU, MR>() ? 512 : 1024)
   constexpr int KBPG = 4 / GPU;                 // k-blocks per group inside a unit
   constexpr bool TABLE = MODE == LUT;
   constexpr bool Z16 = MODE == ZERO_F16;
-  constexpr bool FINE = MODE == ZFINE;          // fine zero-points: B = q - z, scale after
+  constexpr bool FINE = MODE == ZFINE;          // fine zero-points (fp16: B = RN(q - z), scale after)
   constexpr bool HAS_Z = MODE == ZERO_F16 || MODE == ZERO_PACKED || FINE;
   constexpr int REC = (Z16 ? 4 : 2) * GPU;      // scale record bytes per column
   constexpr int SW = REC < 4 ? 1 : REC / 4;     // words per scale record
