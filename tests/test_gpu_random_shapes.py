@@ -4,7 +4,8 @@ M drawn together, so that combinations the structured tests do not list (odd
 tile counts, ragged row blocks, K splits at odd slice counts, two row blocks
 with a partial second one, tables with tiny N ...) meet the oracle as well.
 
-Each case checks wq_dequant_debug bit-exactly and the product through the
+A second set draws deeper and wider layers.  Each case checks
+wq_dequant_debug bit-exactly and the product through the
 entry point linear() picks, plus the other entry point when both accept M,
 against max|y - y_ref| <= 5e-3 * max|y_ref| + 1e-3.
 """
@@ -31,9 +32,9 @@ def wq():
     return m
 
 
-def draw(seed):
+def draw(seed, base=90_000, kmax=2560, nmax_tiles=48, work=120_000_000):
     """One valid random problem (re-drawn until the layer is supported)."""
-    rng = np.random.Generator(np.random.PCG64(90_000 + seed))
+    rng = np.random.Generator(np.random.PCG64(base + seed))
     while True:
         bits = int(rng.choice([2, 3, 4]))
         kt = 256 if bits == 2 else 128
@@ -42,14 +43,14 @@ def draw(seed):
         groups = [-1] + [g for g in (32, 64, 128, 256, 512) if g % kt == 0 or kt % g == 0]
         gs = int(rng.choice(groups))
         unit = kt if gs == -1 else kt * gs // math.gcd(kt, gs)
-        K = unit * int(rng.integers(1, max(2, 2560 // unit) + 1))
-        N = 16 * int(rng.integers(1, 49))
+        K = unit * int(rng.integers(1, max(2, kmax // unit) + 1))
+        N = 16 * int(rng.integers(1, nmax_tiles + 1))
         if mode == wl.ZERO_PACKED and (N * bits) % 32:
             continue
         fine = mode in wl.FINE_ZERO_GROUP
         act_order = bool(gs != -1 and not fine and rng.random() < 0.3)
         M = int(rng.choice(M_CHOICES))
-        if M * N * K > 120_000_000:
+        if M * N * K > work:
             continue
         return dict(bits=bits, mode=mode, dt=dt, gs=gs, K=K, N=N, M=M, act_order=act_order)
 
@@ -58,7 +59,17 @@ def draw(seed):
 # the tolerance when the decode-sized product multiplied unrounded bf16 weights
 @pytest.mark.parametrize("seed", list(range(150)) + [388])
 def test_random_problem(orc, wq, seed):
-    p = draw(seed)
+    check(orc, wq, seed, draw(seed))
+
+
+@pytest.mark.parametrize("seed", range(100))
+def test_random_problem_large(orc, wq, seed):
+    """Deeper and wider layers (K up to 16384, N up to 4096): long k-loops,
+    K splits of many slices, many column blocks."""
+    check(orc, wq, seed, draw(seed, base=70_000, kmax=16384, nmax_tiles=256, work=400_000_000))
+
+
+def check(orc, wq, seed, p):
     print(f"[random] seed={seed} {p}", flush=True)
     L = wl.make_layer(p["K"], p["N"], p["bits"], p["gs"], p["mode"], 500 + seed, act_order=p["act_order"],
                       lut=wl.nf_table(p["bits"]) if p["mode"] == wl.LUT else None)
