@@ -141,7 +141,7 @@ def test_gemm_128_row_tiles(orc, wq, mode, bits, gs, dt):
 
 NARROW_TILE_CASES = [(wl.SYM, 4, 32), (wl.SYM, 2, 128), (wl.ZERO_F16, 4, 64), (wl.ZERO_F16, 2, 256),
                      (wl.ZERO_PACKED, 4, 128), (wl.ZERO_PACKED, 4, 32), (wl.ZERO_PACKED, 3, 64),
-                     (wl.ZERO_PACKED, 2, 256), (wl.LUT, 2, 64), (wl.LUT, 4, 64), (wl.LUT, 4, -1),
+                     (wl.ZERO_PACKED, 2, 256), (wl.ZERO_PACKED, 2, 32), (wl.LUT, 2, 64), (wl.LUT, 4, 64), (wl.LUT, 4, -1),
                      (wl.ZERO_F16_G8, 4, -1), (wl.ZERO_F16_G32, 3, 128)]
 
 
@@ -167,6 +167,23 @@ def test_gemm_128x128_tiles(orc, wq, mode, bits, gs, shapes, dt):
             cols = np.arange(N, dtype=np.int32)
         ok, err, bound = within_tolerance(tensor_f64(y)[:, cols], oracle_y(orc, x_bits, dt, L, cols))
         assert ok, f"K={K} N={N} M={M}: max error {err:.3e} > bound {bound:.3e}"
+
+
+@pytest.mark.parametrize("M", [1, 17, 40, 64])
+@pytest.mark.parametrize("dt", [wl.F16, wl.BF16])
+def test_gemm_2bit_packed_group32_small_m(orc, wq, M, dt):
+    """2-bit codes with packed zero-points in groups of 32 rows take 128 x 128
+    tiles at every M (their 64 x 256 variant would spill): one padded row tile,
+    K split, ragged last column block (N = 528)."""
+    K, N = 1024, 528
+    L = make(wl.ZERO_PACKED, 2, 32, K, N, 9500 + M + dt)
+    layer = repack_layer(wq, L)
+    x_bits = wl.make_x(M, K, dt, 31 + M)
+    print(f"[gemm 2-bit packed g32] M={M} dt={dt}", flush=True)
+    y = wq.wq_gemm(bits_to_tensor(x_bits, act_dtype(dt), "cuda"), layer)
+    torch.cuda.synchronize()
+    ok, err, bound = within_tolerance(tensor_f64(y), oracle_y(orc, x_bits, dt, L))
+    assert ok, f"max error {err:.3e} > bound {bound:.3e}"
 
 
 def test_m_zero_is_a_noop(wq):

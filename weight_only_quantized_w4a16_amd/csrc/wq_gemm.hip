@@ -463,17 +463,25 @@ wq_status run_gemm(GemmArgs g, hipStream_t s) {
   //    tiles more than fill two workgroups per CU: there the doubled LDS
   //    reads of the activations cost more than the decode saves (3-8 %
   //    slower at 768 and more workgroups; 7 % faster at 512).
-  //  * 64 x 256 otherwise (M <= 64 among them).
+  //  * 64 x 256 otherwise (M <= 64 among them), except for the one decode
+  //    below that spills there.
   // The K split (chosen by the host for 64 x 256 workgroups) keeps its slice
   // count whichever tile runs.
   constexpr bool FIT128 = (MODE == SYM && BITS != 2 && (BITS == 3 || GPU <= 2)) ||
                           (MODE == ZERO_F16 && BITS != 2 && GPU == 1) ||
                           (MODE == ZERO_PACKED && BITS == 3 && GPU == 1) ||
                           (MODE == LUT && BITS == 3);
+  // 2-bit codes with packed zero-points in groups of 32 rows spill even at
+  // 64 x 256 (four zero-point words per column tile and unit): 128 x 128 at
+  // every M, 25-90 % faster at M = 8-192 despite the padded rows.
+  constexpr bool NO64 = MODE == ZERO_PACKED && BITS == 2 && GPU == 4;
   const int blocks64 = (g.M + 63) / 64;
   int bm = 64, nt = 4;
   if (FIT128 && g.ksplit == 1 && g.M > 64 && (long)((g.M + 127) / 128) * ((g.N + 255) / 256) >= 480) {
     bm = 128;
+  } else if (NO64) {
+    bm = 128;
+    nt = 2;
   } else if (g.M > 64 && (blocks64 % 2 == 0 || blocks64 >= 7) &&
              !(EPI && (long)blocks64 * ((g.N + 255) / 256) * g.ksplit > 512)) {
     bm = 128;
@@ -484,7 +492,8 @@ wq_status run_gemm(GemmArgs g, hipStream_t s) {
   g.ktps = (g.ktiles + g.ksplit - 1) / g.ksplit;
   const int grid = g.mtiles * g.ntiles_wg * g.ksplit;
   if (bm == 64) {
-    hipLaunchKernelGGL((gemm_kernel<DT, BITS, MODE, GPU, EPI, 64, 4>), dim3(grid), dim3(256), 0, s, g);
+    if constexpr (!NO64)
+      hipLaunchKernelGGL((gemm_kernel<DT, BITS, MODE, GPU, EPI, 64, 4>), dim3(grid), dim3(256), 0, s, g);
   } else if (nt == 2) {
     hipLaunchKernelGGL((gemm_kernel<DT, BITS, MODE, GPU, EPI, 128, 2>), dim3(grid), dim3(256), 0, s, g);
   } else {
