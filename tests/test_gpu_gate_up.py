@@ -110,7 +110,7 @@ def test_gate_up_repack_interleaves_tiles(orc, wq, mode, bits, dt):
 
 GEMV_CASES = [(mode, bits, dt, gs, M, ao)
               for mode in MODES for bits in (2, 3, 4) for dt in (wl.F16, wl.BF16)
-              for gs in (32, 128) for M in (1, 5, 16, 32)
+              for gs in (32, 128) for M in (1, 5, 8, 16, 32)
               for ao in ((False, True) if (gs == 32 and M == 1) else (False,))]
 
 

@@ -68,7 +68,7 @@ def check_product(orc, wq, fn, L, M, dt, seed):
 
 GEMV_CASES = [(mode, bits, dt, gs, M, ao)
               for mode in MODES for bits in (2, 3, 4) for dt in (wl.F16, wl.BF16)
-              for gs in (32, 128, -1) for M in ((1, 3, 5, 16, 17, 32) if gs == 128 else (1, 3, 5, 16, 32))
+              for gs in (32, 128, -1) for M in ((1, 3, 5, 8, 16, 17, 32) if gs == 128 else (1, 3, 5, 8, 16, 32))
               for ao in ((False, True) if (gs == 32 and M in (1, 5, 32)) else (False,))]
 
 

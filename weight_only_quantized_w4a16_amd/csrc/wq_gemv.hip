@@ -22,10 +22,12 @@
 //    With bf16 activations the operand is the dequantised weight itself
 //    (exact product, one rounding to bf16), as in the large-M product.
 //  * M <= 4 packs (row m, k-block kb) into MFMA row 4m + kb, so one 128-bit
-//    activation load feeds the 4 k-blocks of a unit; larger M uses one MFMA
-//    row per activation row (blocks of 16 rows, two for M > 16), loading
-//    either the fragments themselves (M <= 8) or four rows x 256 contiguous
-//    bytes per load, regrouped into fragments through a per-wave LDS stage.
+//    activation load feeds the 4 k-blocks of a unit; M <= 8 packs 8 rows x 2
+//    k-blocks the same way (two loads per unit); larger M uses one MFMA row
+//    per activation row (blocks of 16 rows, two for M > 16), loading four
+//    rows x 256 contiguous bytes per load, regrouped into fragments through a
+//    per-wave LDS stage (the fragments themselves for table codes with four
+//    column tiles per wave).
 //  * Waves reduce through LDS at the end; the output is rounded once.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -93,9 +95,9 @@ constexpr bool gemv_big_frames() { return TN >= 4 || BITS == 2 || (TN >= 2 && GP
 // LDS bytes per wave: the partial results of the cross-wave reduction, or,
 // in the standard scheme, at least the 4 KiB activation stage (the same bytes
 // serve both, one after the other).
-template <int TN, int MR, bool PACKED, bool STAGE>
+template <int TN, int MR, int PK, bool STAGE>
 constexpr int gemv_wave_lds() {
-  constexpr int red = TN * MR * (PACKED ? 1 : 4) * 64 * 4;
+  constexpr int red = TN * MR * (PK == 4 ? 1 : PK == 8 ? 2 : 4) * 64 * 4;
   return STAGE && red < 4096 ? 4096 : red;
 }
 
@@ -106,12 +108,15 @@ constexpr int gemv_wave_lds() {
 // MR: blocks of 16 activation rows (standard scheme; M <= 16 MR).
 // STAGE: standard scheme with contiguous activation loads regrouped through
 // the wave's LDS stage (otherwise the fragments are loaded directly).
-template <int DT, int BITS, int MODE, int TN, int GPU, bool PACKED, int PF, bool SWIGLU, int MR, bool STAGE>
+// PK: packed scheme with 4 rows x 4 k-blocks (PK = 4) or 8 rows x 2 k-blocks
+// (PK = 8) in the 16 MFMA rows; 0: standard scheme.
+template <int DT, int BITS, int MODE, int TN, int GPU, int PK, int PF, bool SWIGLU, int MR, bool STAGE>
 __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU, MR>() ? 512 : 1024)) void gemv_kernel(const GemvArgs a) {
+  constexpr bool PACKED = PK != 0;
   constexpr int KT = BITS == 2 ? 256 : 128;
   constexpr int UPT = KT / 128;                 // 128-row units per tile
   constexpr int WPL = BITS == 3 ? 3 : 4;
-  constexpr int NXA = PACKED ? UPT : 4 * UPT;   // activation loads per tile
+  constexpr int NXA = PK == 4 ? UPT : PK == 8 ? 2 * UPT : 4 * UPT;  // activation loads per tile
   constexpr int KBPG = 4 / GPU;                 // k-blocks per group inside a unit
   constexpr bool TABLE = MODE == LUT;
   constexpr bool Z16 = MODE == ZERO_F16;
@@ -123,16 +128,16 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU, MR>() ? 512 : 1024)
   constexpr bool SCALED = DT == BF16;          // decoded weights already carry the scale
   constexpr bool XS = !SCALED && MODE != LUT && !FINE;  // shared zero-points: remove bias + z via row sums
   constexpr int ZW = FINE ? 2 : (HAS_Z && !Z16 ? GPU : 1);  // words of a zero record
-  constexpr int NRED = PACKED ? 1 : 4;          // reduced values per lane per column tile
+  constexpr int NRED = PK == 4 ? 1 : PK == 8 ? 2 : 4;  // reduced values per lane per column tile
 
   __shared__ uint32_t table[TABLE ? (32 << (2 * BITS)) : 1];
   // LDS of wave w at red + w * WSTRIDE: its activation stage (standard scheme,
   // 4 KiB) while it streams, then its partial results [TN][MR][NRED][64] for
   // the cross-wave reduction.
   extern __shared__ float red[];
-  constexpr int WSTRIDE = gemv_wave_lds<TN, MR, PACKED, STAGE>() / 4;  // floats
+  constexpr int WSTRIDE = gemv_wave_lds<TN, MR, PK, STAGE>() / 4;  // floats
   static_assert(!STAGE || !PACKED, "the packed scheme loads its fragments directly");
-  static_assert(!PACKED || MR == 1, "the packed scheme holds at most 4 rows");
+  static_assert(!PACKED || MR == 1, "the packed scheme holds at most 8 rows");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar arithmetic
@@ -149,6 +154,8 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU, MR>() ? 512 : 1024)
   // part becomes kOutOfRange for loads that must return zero (rows past M,
   // tiles past the wave's range).
   //   packed:   lane c -> (m = c / 4, k-block c % 4), one load per 128-row unit;
+  //   packed 8: lane c -> (m = c / 2, k-block 2 p + c % 2), load p = 0, 1 of a
+  //             unit covering its k-blocks 2 p and 2 p + 1;
   //   standard: lane c -> m = 16 r + c, one load per k-block (the MFMA
   //             fragment itself: 16 rows, half a cache line each, per load);
   //   staged:   load j of a unit and row block r reads rows 16 r + 4 j .. + 3,
@@ -161,8 +168,8 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU, MR>() ? 512 : 1024)
   for (int r = 0; r < MR; ++r)
 #pragma unroll
     for (int j = 0; j < XJ; ++j) {
-      const int xm = PACKED ? (c >> 2) : STAGE ? 16 * r + 4 * j + h : 16 * r + c;
-      const int xk = PACKED ? 8 * h + 32 * (c & 3) : STAGE ? 8 * c : 8 * h;
+      const int xm = PK == 4 ? (c >> 2) : PK == 8 ? (c >> 1) : STAGE ? 16 * r + 4 * j + h : 16 * r + c;
+      const int xk = PK == 4 ? 8 * h + 32 * (c & 3) : PK == 8 ? 8 * h + 32 * (c & 1) : STAGE ? 8 * c : 8 * h;
       x_lane[r][j] = xm < a.M ? (uint32_t)(xm * a.K + xk) * 2u : kOutOfRange;
     }
   // LDS stage of this wave: row i (0..15) of the unit at 16 chunks of 16 bytes,
@@ -214,10 +221,12 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU, MR>() ? 512 : 1024)
     for (int r = 0; r < MR; ++r) {
 #pragma unroll
       for (int i = 0; i < NXA; ++i) {
-        // packed: load i covers unit i; standard: k-block i; staged: load
-        // j = i % 4 of unit i / 4
+        // packed: load i covers unit i; packed 8: half i % 2 of unit i / 2;
+        // standard: k-block i; staged: load j = i % 4 of unit i / 4
         const uint32_t xv = ok ? x_lane[r][STAGE ? i % 4 : 0] : kOutOfRange;
-        const uint32_t koff = (uint32_t)(ktc * KT + (PACKED ? 128 * i : STAGE ? 128 * (i / 4) : 32 * i)) * 2u;
+        const uint32_t koff =
+            (uint32_t)(ktc * KT + (PK == 4 ? 128 * i : PK == 8 ? 128 * (i / 2) + 64 * (i % 2)
+                                  : STAGE ? 128 * (i / 4) : 32 * i)) * 2u;
         f.xa[r][i] = __builtin_amdgcn_raw_buffer_load_b128(rx, xv, koff, 0);
       }
     }
@@ -272,7 +281,42 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU, MR>() ? 512 : 1024)
     const f4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
     sfor<UPT>([&](auto uc) {
       constexpr int u = decltype(uc)::value;
-      if constexpr (PACKED) {
+      if constexpr (PK == 8) {
+        // Two A operands per unit (p = 0, 1: rows 2m + j hold k-block 2p + j);
+        // accumulator kb keeps the rows 2m + kb % 2, i.e. the elements e with
+        // e % 2 == kb % 2 (row 4h + e = 2m + j: m = 2h + e / 2, j = e % 2).
+        f4 acc[TN][4];
+        sfor<4>([&](auto kbc) {
+          constexpr int kb = decltype(kbc)::value;
+#pragma unroll
+          for (int t = 0; t < TN; ++t) {
+            const u32x4 b = decode_frag<BITS, DT, MODE, 4 * u + kb>(
+                f.w[t], tab, dk, FINE ? fine_zero_bits(f.z[t][u], kb) : 0u,
+                SCALED ? rec_scale<Z16>(f.s[t][u], kb / KBPG) : 0.0f,
+                SCALED && !TABLE && !FINE ? zero_of(f, t, u, kb / KBPG) : 0.0f);
+            acc[t][kb] = mfma16<DT>(f.xa[0][2 * u + kb / 2], b, zero4);
+          }
+        });
+        f4 xs[2] = {zero4, zero4};
+        if constexpr (XS) {
+#pragma unroll
+          for (int p = 0; p < 2; ++p) xs[p] = mfma16<DT>(f.xa[0][2 * u + p], ones_frag<DT>(), zero4);
+        }
+#pragma unroll
+        for (int t = 0; t < TN; ++t) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+#pragma unroll
+            for (int kb = e & 1; kb < 4; kb += 2) {
+              const int j = kb / KBPG;
+              const float s = SCALED ? 1.0f : rec_scale<Z16>(f.s[t][u], j);
+              float v = acc[t][kb][e];
+              if constexpr (XS) v = __builtin_fmaf(-zero_corr<DT>(zero_of(f, t, u, j)), xs[kb / 2][e], v);
+              tot[0][t][e] = __builtin_fmaf(s, v, tot[0][t][e]);
+            }
+          }
+        }
+      } else if constexpr (PACKED) {
         // One A operand for the 4 k-blocks of the unit; accumulator kb keeps row 4m + kb.
         f4 acc[TN][4];
         sfor<4>([&](auto kbc) {
@@ -391,7 +435,10 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU, MR>() ? 512 : 1024)
 #pragma unroll
     for (int r = 0; r < MR; ++r) {
       float* dst = red + (size_t)wave * WSTRIDE + (size_t)((t * MR + r) * NRED) * 64;
-      if constexpr (PACKED) {
+      if constexpr (PK == 8) {
+        dst[lane] = tot[r][t][0] + tot[r][t][1];       // row 2h
+        dst[64 + lane] = tot[r][t][2] + tot[r][t][3];  // row 2h + 1
+      } else if constexpr (PACKED) {
         dst[lane] = (tot[r][t][0] + tot[r][t][1]) + (tot[r][t][2] + tot[r][t][3]);
       } else {
 #pragma unroll
@@ -416,8 +463,9 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU, MR>() ? 512 : 1024)
     } else {
       v = reduce(0, 1);
     }
-    // packed: lane l = 16 m + col ; standard: row 16 rb + 4 (l / 16) + e, col l % 16
-    const int m = PACKED ? (l >> 4) : 16 * rb + 4 * (l >> 4) + e;
+    // packed: lane l = 16 m + col; packed 8: row 2 (l / 16) + e, col l % 16;
+    // standard: row 16 rb + 4 (l / 16) + e, col l % 16
+    const int m = PK == 4 ? (l >> 4) : PK == 8 ? 2 * (l >> 4) + e : 16 * rb + 4 * (l >> 4) + e;
     const int n = (SWIGLU ? (int)blockIdx.x : nt0 + t) * 16 + (l & 15);
     if (m < a.M) a.y[(size_t)m * a.ldy + n] = DT == F16 ? f32_to_f16(v) : f32_to_bf16(v);
   }
@@ -426,10 +474,10 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU, MR>() ? 512 : 1024)
 // ---------------------------------------------------------------------------
 // Launch-shape choice and dispatch.
 // ---------------------------------------------------------------------------
-template <int DT, int BITS, int MODE, int TN, int GPU, bool PACKED, int PF, bool SWIGLU, int MR, bool STAGE>
+template <int DT, int BITS, int MODE, int TN, int GPU, int PK, int PF, bool SWIGLU, int MR, bool STAGE>
 wq_status run(GemvArgs g, int grid, hipStream_t s) {
-  const size_t lds = (size_t)g.waves * gemv_wave_lds<TN, MR, PACKED, STAGE>();
-  hipLaunchKernelGGL((gemv_kernel<DT, BITS, MODE, TN, GPU, PACKED, PF, SWIGLU, MR, STAGE>), dim3(grid), dim3(g.waves * 64),
+  const size_t lds = (size_t)g.waves * gemv_wave_lds<TN, MR, PK, STAGE>();
+  hipLaunchKernelGGL((gemv_kernel<DT, BITS, MODE, TN, GPU, PK, PF, SWIGLU, MR, STAGE>), dim3(grid), dim3(g.waves * 64),
                      lds, s, g);
   return launch_status();
 }
@@ -447,27 +495,26 @@ inline int pick_waves(int grid, int ktiles, bool table, int wmax, long plain = 3
   while (w < wmax && 2 * w <= ktiles && ((long)grid * w < target || ktiles > 32 * w)) w *= 2;
   return w;
 }
-template <int DT, int BITS, int MODE, int TN, int GPU, bool PACKED, bool SWIGLU, int MR, bool STAGE = false>
+template <int DT, int BITS, int MODE, int TN, int GPU, int PK, bool SWIGLU, int MR, bool STAGE = false>
 wq_status run_pf(GemvArgs g, int grid, hipStream_t s) {
   const int tpw = g.kt_per_wave;
-  if constexpr (PACKED) {
-    if (tpw >= 8) return run<DT, BITS, MODE, TN, GPU, PACKED, 4, SWIGLU, MR, false>(g, grid, s);
-    if (tpw >= 5) return run<DT, BITS, MODE, TN, GPU, PACKED, 3, SWIGLU, MR, false>(g, grid, s);
+  if constexpr (PK != 0) {
+    if (tpw >= 8) return run<DT, BITS, MODE, TN, GPU, PK, 4, SWIGLU, MR, false>(g, grid, s);
+    if (tpw >= 5) return run<DT, BITS, MODE, TN, GPU, PK, 3, SWIGLU, MR, false>(g, grid, s);
   }
-  return run<DT, BITS, MODE, TN, GPU, PACKED, 2, SWIGLU, MR, STAGE>(g, grid, s);
+  return run<DT, BITS, MODE, TN, GPU, PK, 2, SWIGLU, MR, STAGE>(g, grid, s);
 }
 
-// Standard scheme (one activation row per MFMA row, MR blocks of 16 rows).
-// Activations go through the LDS stage for more than 8 rows (measured on the
-// decode layer shapes: 5-38 % faster at 16 rows, up to 5 % slower at 5),
-// except with four column tiles per wave and table codes, whose LDS table
-// and stage together cost occupancy.
+// Standard scheme (one activation row per MFMA row, MR blocks of 16 rows,
+// more than 8 rows).  Activations go through the LDS stage (measured on the
+// decode layer shapes: 5-38 % faster at 16 rows), except with four column
+// tiles per wave and table codes, whose LDS table and stage together cost
+// occupancy.
 template <int DT, int BITS, int MODE, int TN, int GPU, bool SWIGLU, int MR>
 wq_status run_standard(GemvArgs g, int grid, hipStream_t s) {
-  const bool stage = MR == 2 || (g.M > 8 && !(MODE == LUT && TN == 4));
-  if constexpr (MR == 1)
-    if (!stage) return run_pf<DT, BITS, MODE, TN, GPU, false, SWIGLU, MR, false>(g, grid, s);
-  return run_pf<DT, BITS, MODE, TN, GPU, false, SWIGLU, MR, true>(g, grid, s);
+  constexpr bool stage = MR == 2 || !(MODE == LUT && TN == 4);
+  if constexpr (!stage) return run_pf<DT, BITS, MODE, TN, GPU, 0, SWIGLU, MR, false>(g, grid, s);
+  else return run_pf<DT, BITS, MODE, TN, GPU, 0, SWIGLU, MR, true>(g, grid, s);
 }
 
 template <int DT, int BITS, int MODE, int GPU, bool SWIGLU, int MR>
@@ -530,18 +577,23 @@ wq_status pick_shape(GemvArgs g, hipStream_t s) {
       return pick_standard<DT, BITS, MODE, GPU, SWIGLU, 2>(g, s);
     }
   }
-  if (g.M > 4) return pick_standard<DT, BITS, MODE, GPU, SWIGLU, 1>(g, s);
-  // Packed scheme: M <= 4 rows x 4 k-blocks in the 16 MFMA rows.
+  if (g.M > 8) return pick_standard<DT, BITS, MODE, GPU, SWIGLU, 1>(g, s);
+  // Packed scheme: M <= 4 rows x 4 k-blocks, or M <= 8 rows x 2 k-blocks, in
+  // the 16 MFMA rows (8 rows: 8-35 % faster at M = 5-8 than the standard
+  // scheme, whose MFMA rows are half empty there).
   const int wmax = gemv_big_frames<BITS, 1, GPU, 1>() ? 8 : 16;
+  const bool pk8 = g.M > 4;
   if constexpr (SWIGLU) {
     const int kw = max(1, pick_waves(ntiles, g.ktiles, MODE == LUT, wmax) / 2);  // waves per column tile
     g.waves = 2 * kw;
     g.kt_per_wave = (g.ktiles + kw - 1) / kw;
-    return run_pf<DT, BITS, MODE, 1, GPU, true, true, 1>(g, ntiles / 2, s);
+    return pk8 ? run_pf<DT, BITS, MODE, 1, GPU, 8, true, 1>(g, ntiles / 2, s)
+               : run_pf<DT, BITS, MODE, 1, GPU, 4, true, 1>(g, ntiles / 2, s);
   } else {
     g.waves = pick_waves(ntiles, g.ktiles, MODE == LUT, wmax);
     g.kt_per_wave = (g.ktiles + g.waves - 1) / g.waves;
-    return run_pf<DT, BITS, MODE, 1, GPU, true, false, 1>(g, ntiles, s);
+    return pk8 ? run_pf<DT, BITS, MODE, 1, GPU, 8, false, 1>(g, ntiles, s)
+               : run_pf<DT, BITS, MODE, 1, GPU, 4, false, 1>(g, ntiles, s);
   }
 }
 
