@@ -600,7 +600,9 @@ wq_status pick_shape(GemvArgs g, hipStream_t s) {
     return pk8 ? run_pf<DT, BITS, MODE, 1, GPU, 8, true, 1>(g, ntiles / 2, s)
                : run_pf<DT, BITS, MODE, 1, GPU, 4, true, 1>(g, ntiles / 2, s);
   } else {
-    g.waves = pick_waves(ntiles, g.ktiles, MODE == LUT, wmax);
+    // about 4096 waves (3072 measured 3-10 % slower on the 12288-, 24576- and
+    // 28672-column layers, equal elsewhere)
+    g.waves = pick_waves(ntiles, g.ktiles, MODE == LUT, wmax, 4096L);
     g.kt_per_wave = (g.ktiles + g.waves - 1) / g.waves;
     return pk8 ? run_pf<DT, BITS, MODE, 1, GPU, 8, false, 1>(g, ntiles, s)
                : run_pf<DT, BITS, MODE, 1, GPU, 4, false, 1>(g, ntiles, s);
