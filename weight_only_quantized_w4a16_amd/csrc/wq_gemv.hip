@@ -482,10 +482,11 @@ wq_status run(GemvArgs g, int grid, hipStream_t s) {
   return launch_status();
 }
 
-// Launch shape (measured on MI355X for the decode layer shapes): about 3072
-// waves over the grid, each streaming an equal share of K; the prefetch depth
-// grows with the tiles a wave streams (deeper prefetch costs registers and
-// out-of-range tail loads, so short ranges keep it at 2).
+// Launch shape (measured on MI355X for the decode layer shapes): a few
+// thousand waves over the grid (about 4096 for the packed schemes, 3072 for
+// one block of 16 rows, 1536 for two), each streaming an equal share of K;
+// the prefetch depth grows with the tiles a wave streams (deeper prefetch
+// costs registers and out-of-range tail loads, so short ranges keep it at 2).
 inline int pick_waves(int grid, int ktiles, bool table, int wmax, long plain = 3072L) {
   // about `plain` waves in flight (12288 when each workgroup fills an LDS code
   // table, which caps the workgroups per CU), at most 32 k-tiles per wave,
