@@ -254,8 +254,9 @@ def run_points(args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: every box here has one, and this product path is "
-              f"single-GPU (asked for --gpus {args.gpus}).", file=sys.stderr)
+        print(f"bench.py measures one GPU: the product path runs on a single GPU (asked for "
+              f"--gpus {args.gpus}); how it would shard over several is a design note only.",
+              file=sys.stderr)
         sys.exit(2)
     if args.points:
         run_points(args)

@@ -185,3 +185,14 @@ def test_size_limits(L):
     assert call_product(L, "wq_gemv", K=65536, N=65536) == 2
     # activations: M*K*2 bytes must stay below 2 GiB
     assert call_product(L, "wq_gemm", M=1 << 18, K=4096) == 2
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The benchmark measures one GPU and says so for any other count (it
+    exits before touching a GPU)."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
