@@ -47,7 +47,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, TFLOP/s
 METRIC = "weight GB/s (GEMV, M=1) & TFLOP/s (GEMM, M=2048) as % of HBM/MFMA roofline"
-KERNEL_SOURCES = ["wq_gemv.hip", "wq_decode.hpp", "wq_layout.hpp"]
+KERNEL_SOURCES = ["wq_gemv.hip", "wq_decode.hpp", "wq_layout.hpp"]  # the dominant (GEMV) kernel's sources
+ALL_SOURCES = ["wq_api.hip", "wq_common.hpp", "wq_decode.hpp", "wq_gemm.hip", "wq_gemv.hip", "wq_hadamard.hip",
+               "wq_layout.hpp"]
 
 
 def parse():
@@ -72,12 +74,22 @@ def parse():
                         "groups of the workloads) against its roofline, plus context numbers")
     p.add_argument("--points-configs", default="1,2,3,4,5,6",
                    help="configurations for --points (comma-separated ids)")
+    p.add_argument("--points-only", nargs="*", default=[],
+                   help="restrict --points to cases cid/layer/bits/M-list ('*' matches any), "
+                        "e.g. 5/wide/4/1,2 4/up/*/1")
+    p.add_argument("--no-read-ceiling", action="store_true",
+                   help="--points: skip the streaming-read ceiling of each M=1 point")
+    p.add_argument("--profile-case", nargs="*", default=[],
+                   help="instead of the step: launch only these products back to back, each "
+                        "cid/layer/bits/group/M (e.g. 5/wide/4/32/1), for rocprofv3 runs; 'copy' "
+                        "adds a 256 MiB device copy (counter calibration)")
+    p.add_argument("--profile-reps", type=int, default=40)
     return p.parse_args()
 
 
-def kernel_hash():
+def kernel_hash(files=KERNEL_SOURCES):
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, "weight_only_quantized_w4a16_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -102,105 +114,246 @@ def read_traffic(khash):
         return None
 
 
+class Dev:
+    """Moves seeded workload arrays to cuda:0 and repacks layers (no timing)."""
+
+    def __init__(self):
+        import torch
+
+        import weight_only_quantized_w4a16_amd as wq
+
+        self.torch, self.wq = torch, wq
+        self.dev = torch.device("cuda:0")
+
+    def t(self, a, dtype):
+        import numpy as np
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return self.torch.from_numpy(a.view(np.int16)).view(dtype).to(self.dev)
+        return self.torch.from_numpy(a.view(np.int32)).to(self.dev)
+
+    def repack(self, L, copies=1, fn=None):
+        import workloads as wl
+        torch, wq = self.torch, self.wq
+        fn = fn or wq.wq_repack
+        q = self.t(L.qweight, torch.int32)
+        sc = self.t(L.scales, torch.float16)
+        z = None
+        if L.mode == wl.ZERO_F16 or L.mode in wl.FINE_ZERO_GROUP:
+            z = self.t(L.zeros, torch.float16)
+        elif L.mode == wl.ZERO_PACKED:
+            z = self.t(L.zeros, torch.int32)
+        lut = self.t(L.lut, torch.float16) if L.lut is not None else None
+        out = [fn(q, sc, z, L.mode, L.g_idx, L.K, L.N, L.bits, L.group_size, lut=lut) for _ in range(copies)]
+        del q, sc, z
+        return out
+
+
+def graph_time(stream, fn, n, replays=5):
+    """fn(i) launches call i on `stream`; n calls captured in one HIP graph;
+    median over `replays` replays of the GPU time per call, in us."""
+    import statistics
+
+    import torch
+    with torch.cuda.stream(stream):
+        for i in range(n):
+            fn(i)
+    stream.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(n):
+                fn(i)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        g.replay()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(replays):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):  # replay() launches on the current stream
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) / n * 1e3)
+    del g
+    return statistics.median(ts)
+
+
+_probe = None
+
+
+def probe_lib():
+    """libwq_probe.so (the streaming-read probe, include/wq_probe.h)."""
+    global _probe
+    if _probe is None:
+        import ctypes
+
+        from weight_only_quantized_w4a16_amd import build as wq_build
+        if not os.path.exists(wq_build.PROBE_LIB):
+            raise RuntimeError(f"{wq_build.PROBE_LIB} is not built")
+        L = ctypes.CDLL(wq_build.PROBE_LIB)
+        L.wq_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_void_p, ctypes.c_void_p]
+        L.wq_probe_stream_read.restype = ctypes.c_int
+        _probe = L
+    return _probe
+
+
+def read_ceiling(stream, bufs, nbytes, n):
+    """The fastest one launch reads `nbytes` bytes: the streaming-read probe
+    over the rotated buffers `bufs` (same protocol as the product: n launches
+    per graph replay, median of 5), best over a sweep of workgroup counts and
+    loads in flight.  Returns (us per launch, GB/s, best launch shape)."""
+    import torch
+    L = probe_lib()
+    nbytes = nbytes // 16 * 16
+    sink = torch.zeros(4, dtype=torch.uint8, device=bufs[0].device)
+    best = None
+    for wgs in (512, 1024, 2048, 4096, 8192):
+        for u in (4, 8):
+            def call(i):
+                rc = L.wq_probe_stream_read(bufs[i % len(bufs)].data_ptr(), nbytes, wgs, u, sink.data_ptr(),
+                                            stream.cuda_stream)
+                if rc != 0:
+                    raise RuntimeError(f"wq_probe_stream_read failed ({rc})")
+            us = graph_time(stream, call, n)
+            if best is None or us < best[0]:
+                best = (us, wgs, u)
+    us, wgs, u = best
+    return us, nbytes / us / 1e3, {"workgroups": wgs, "loads_in_flight": u}
+
+
+def run_profile_cases(args):
+    """Only the named products (and an optional device copy of known size),
+    each launched --profile-reps times back to back over rotated copies of its
+    layer: the workload of the committed rocprofv3 summaries, one process per
+    counter pass, so every dispatch of a kernel in the run belongs to one case."""
+    import torch
+
+    import workloads as wl
+    d = Dev()
+    wq = d.wq
+    wq.lib()
+    torch.cuda.set_device(d.dev)
+    stream = torch.cuda.current_stream()
+    for spec in args.profile_case:
+        if spec == "copy":
+            src = torch.empty(1 << 28, dtype=torch.uint8, device=d.dev).fill_(1)
+            dst = torch.empty_like(src)
+            for _ in range(5):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            print(json.dumps({"case": "copy", "bytes": 1 << 28, "calls": 5}), flush=True)
+            del src, dst
+            continue
+        cid, lname, bits, gs, M = spec.split("/")
+        cfg = wl.CONFIGS[int(cid)]
+        L = cfg.layer(lname, int(bits), int(gs))
+        M = int(M)
+        wb = L.weight_bytes()
+        R = max(2, -(-(1 << 30) // wb))
+        copies = d.repack(L, R)
+        tdt = torch.float16 if cfg.dtype == wl.F16 else torch.bfloat16
+        x = d.t(cfg.x(M, L.K), tdt)
+        y = torch.empty((M, L.N), dtype=tdt, device=d.dev)
+        ws = torch.empty(max(wq.wq_workspace_bytes(M, L.N, L.K, L.bits, copies[0].perm is not None), 16),
+                         dtype=torch.uint8, device=d.dev)
+        for i in range(R):
+            wq.linear(x, copies[i], out=y, ws=ws, stream=stream)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.profile_reps):
+            wq.linear(x, copies[i % R], out=y, ws=ws, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        print(json.dumps({"case": spec, "path": "gemv" if wq.use_gemv(M, copies[0]) else "gemm",
+                          "calls": args.profile_reps, "rotated_copies": R, "weight_bytes": wb,
+                          "us_per_call_event_timed": round(e0.elapsed_time(e1) / args.profile_reps * 1e3, 3)}),
+              flush=True)
+        del copies, x, y, ws
+        torch.cuda.empty_cache()
+
+
+def _match(spec, cid, lname, bits, M):
+    f = spec.split("/") + ["*"] * 4
+    return ((f[0] in ("*", str(cid))) and (f[1] in ("*", lname)) and (f[2] in ("*", str(bits)))
+            and (f[3] == "*" or str(M) in f[3].split(",")))
+
+
 def run_points(args):
     """Every configuration point (layer shape x M x code width x group) through
     the product entry point a caller uses (linear(): the GEMV for decode-sized M,
     the GEMM above), timed as back-to-back launches over R rotated copies of the
     layer (R x weight bytes > 1 GiB) captured in a HIP graph and replayed; the
     median of 5 replays.  Each point is set against t_ideal = max(algorithmic
-    bytes / 8 TB/s, 2MNK / 2.5 PFLOP/s).  Context: single-call latency with a
-    cold last-level cache (512 MB written in between), torch's own streaming
-    read and copy over 2 GiB, and torch.matmul in fp16 on weights dequantised
-    at load time (wq_dequant_debug) at the prefill shapes."""
+    bytes / 8 TB/s, 2MNK / 2.5 PFLOP/s), and each M = 1 point against the
+    streaming-read ceiling of its weight bytes (the probe kernel reading the
+    same rotated buffers under the same protocol).  Context: single-call latency
+    with a cold last-level cache (512 MB written in between), torch's own
+    streaming read and copy over 2 GiB, and torch.matmul in fp16 on weights
+    dequantised at load time (wq_dequant_debug) at the prefill shapes."""
     import statistics
 
-    import numpy as np
     import torch
 
-    import weight_only_quantized_w4a16_amd as wq
     import workloads as wl
 
+    d = Dev()
+    wq = d.wq
     wq.lib()
-    dev = torch.device("cuda:0")
+    dev = d.dev
     torch.cuda.set_device(dev)
     s = torch.cuda.Stream()
-
-    def to_dev(a, dtype):
-        a = np.ascontiguousarray(a)
-        if a.dtype == np.uint16:
-            return torch.from_numpy(a.view(np.int16)).view(dtype).to(dev)
-        return torch.from_numpy(a.view(np.int32)).to(dev)
-
-    def repack(L):
-        q = to_dev(L.qweight, torch.int32)
-        sc = to_dev(L.scales, torch.float16)
-        z = None
-        if L.mode == wl.ZERO_F16 or L.mode in wl.FINE_ZERO_GROUP:
-            z = to_dev(L.zeros, torch.float16)
-        elif L.mode == wl.ZERO_PACKED:
-            z = to_dev(L.zeros, torch.int32)
-        lut = to_dev(L.lut, torch.float16) if L.lut is not None else None
-        return wq.wq_repack(q, sc, z, L.mode, L.g_idx, L.K, L.N, L.bits, L.group_size, lut=lut)
-
-    def graph_time(fn, n):
-        """fn(i) launches call i on stream s; n calls per replay; median us per call."""
-        with torch.cuda.stream(s):
-            for i in range(n):
-                fn(i)
-        s.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(s):
-            with torch.cuda.graph(g, stream=s):
-                for i in range(n):
-                    fn(i)
-        torch.cuda.synchronize()
-        with torch.cuda.stream(s):
-            g.replay()
-        torch.cuda.synchronize()
-        ts = []
-        for _ in range(5):
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            with torch.cuda.stream(s):  # replay() launches on the current stream
-                e0.record(s)
-                g.replay()
-                e1.record(s)
-            torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1) / n * 1e3)
-        del g
-        return statistics.median(ts)
 
     scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     points, cold = [], []
     want = {int(c) for c in args.points_configs.split(",")}
+    only = args.points_only
     for cid, cfg in wl.CONFIGS.items():
         if cid not in want:
             continue
         tdt = torch.float16 if cfg.dtype == wl.F16 else torch.bfloat16
         for (lname, K, N) in cfg.layers:
             for bits in cfg.bits:
+                Ms = [M for M in cfg.Ms if not only or any(_match(sp, cid, lname, bits, M) for sp in only)]
+                if not Ms:
+                    continue
                 for gs in cfg.groups:
                     L = cfg.layer(lname, bits, gs)
                     wb = L.weight_bytes()
                     R = max(2, -(-(1 << 30) // wb))
-                    copies = [repack(L) for _ in range(R)]
-                    for M in cfg.Ms:
-                        x = to_dev(cfg.x(M, K), tdt)
+                    copies = d.repack(L, R)
+                    n = R * max(1, -(-8 // R))
+                    ceiling = None
+                    if 1 in Ms and not args.no_read_ceiling:
+                        nbytes = min(wb, copies[0].packed.numel())
+                        r_us, r_gbs, shape = read_ceiling(s, [c.packed for c in copies], nbytes, n)
+                        ceiling = {"read_us": round(r_us, 2), "read_GBps": round(r_gbs, 1), "bytes": nbytes,
+                                   "shape": shape}
+                    for M in Ms:
+                        x = d.t(cfg.x(M, K), tdt)
                         y = torch.empty((M, N), dtype=tdt, device=dev)
                         has_perm = copies[0].perm is not None
                         ws = torch.empty(max(wq.wq_workspace_bytes(M, N, K, bits, has_perm), 16),
                                          dtype=torch.uint8, device=dev)
                         path = "gemv" if wq.use_gemv(M, copies[0]) else "gemm"
-                        n = R * max(1, -(-8 // R))
-                        us = graph_time(lambda i: wq.linear(x, copies[i % R], out=y, ws=ws, stream=s), n)
+                        us = graph_time(s, lambda i: wq.linear(x, copies[i % R], out=y, ws=ws, stream=s), n)
                         flops = 2.0 * M * N * K
                         alg = wb + 2 * M * K + 2 * M * N + (4 * K if has_perm else 0)
                         t_ideal = max(alg / (HBM_PEAK_GBS * 1e3), flops / (MFMA_F16_PEAK_TFLOPS * 1e6))
-                        points.append({"config": cfg.name, "layer": f"{lname} {K}x{N}", "bits": bits,
-                                       "group": gs, "M": M, "path": path, "us": round(us, 2),
-                                       "weight_GBps": round(wb / us / 1e3, 1),
-                                       "tflops": round(flops / us / 1e6, 1),
-                                       "t_ideal_us": round(t_ideal, 2), "frac_of_ideal": round(t_ideal / us, 3)})
+                        pt = {"config": cfg.name, "layer": f"{lname} {K}x{N}", "bits": bits, "group": gs, "M": M,
+                              "path": path, "us": round(us, 2), "weight_GBps": round(wb / us / 1e3, 1),
+                              "tflops": round(flops / us / 1e6, 1), "t_ideal_us": round(t_ideal, 2),
+                              "frac_of_ideal": round(t_ideal / us, 3)}
+                        if M == 1 and ceiling is not None:
+                            pt["read_ceiling"] = ceiling
+                            pt["frac_of_read_ceiling"] = round(ceiling["read_us"] / us, 3)
+                        points.append(pt)
                         print(f"[points] {points[-1]}", file=sys.stderr, flush=True)
                         if M == 1 and cid in (1, 2):
                             # one call after 512 MB of writes (the last-level cache holds none of it)
@@ -221,33 +374,37 @@ def run_points(args):
                     del copies
                     torch.cuda.empty_cache()
     del scratch
-    # torch's own streaming kernels over 2 GiB (context for what a read can reach)
-    big = torch.empty(1 << 31, dtype=torch.uint8, device=dev).fill_(1)
-    dst = torch.empty_like(big)
-    v = big.view(torch.float32)  # 0x01010101: a normal float
-    read_us = graph_time(lambda i: v.sum(), 4)
-    copy_us = graph_time(lambda i: dst.copy_(big), 4)
-    del big, dst, v
-    torch.cuda.empty_cache()
-    stream_ctx = {"bytes": 1 << 31, "torch_f32_sum_read_GBps": round((1 << 31) / read_us / 1e3, 1),
-                  "torch_copy_read_plus_write_GBps": round(2 * (1 << 31) / copy_us / 1e3, 1)}
+    ctx = {}
+    if not only:
+        # torch's own streaming kernels over 2 GiB (context for what a read can reach)
+        big = torch.empty(1 << 31, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(big)
+        v = big.view(torch.float32)  # 0x01010101: a normal float
+        read_us = graph_time(s, lambda i: v.sum(), 4)
+        copy_us = graph_time(s, lambda i: dst.copy_(big), 4)
+        probe_us, probe_gbs, shape = read_ceiling(s, [big], 1 << 31, 4)
+        del big, dst, v
+        torch.cuda.empty_cache()
+        ctx = {"bytes": 1 << 31, "torch_f32_sum_read_GBps": round((1 << 31) / read_us / 1e3, 1),
+               "torch_copy_read_plus_write_GBps": round(2 * (1 << 31) / copy_us / 1e3, 1),
+               "probe_read_GBps": round(probe_gbs, 1), "probe_shape": shape}
     # dense fp16 comparator: torch.matmul on weights dequantised at load time
     dense = []
-    if 3 in want:
+    if 3 in want and not only:
         c3 = wl.CONFIGS[3]
         for (lname, K, N) in c3.layers:
-            layer = repack(c3.layer(lname, 4, -1))
+            layer = d.repack(c3.layer(lname, 4, -1))[0]
             W = wq.wq_dequant_debug(layer, torch.float16)
             del layer
             for M in c3.Ms:
-                x = to_dev(c3.x(M, K), torch.float16)
+                x = d.t(c3.x(M, K), torch.float16)
                 y = torch.empty((M, N), dtype=torch.float16, device=dev)
-                us = graph_time(lambda i: torch.matmul(x, W, out=y), 4)
+                us = graph_time(s, lambda i: torch.matmul(x, W, out=y), 4)
                 dense.append({"layer": f"{lname} {K}x{N}", "M": M, "us": round(us, 2),
                               "tflops": round(2.0 * M * N * K / us / 1e6, 1)})
             del W
             torch.cuda.empty_cache()
-    print(json.dumps({"points": points, "cold_single_call": cold, "stream_2GiB": stream_ctx,
+    print(json.dumps({"points": points, "cold_single_call": cold, "stream_2GiB": ctx,
                       "dense_fp16_torch_matmul": dense}))
 
 
@@ -260,6 +417,9 @@ def main():
         sys.exit(2)
     if args.points:
         run_points(args)
+        return
+    if args.profile_case:
+        run_profile_cases(args)
         return
 
     import numpy as np

@@ -196,3 +196,25 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_probe_library_exports_its_header():
+    """libwq_probe.so (measurement probe, include/wq_probe.h) exports what it declares."""
+    import ctypes
+
+    from weight_only_quantized_w4a16_amd import build
+    if not os.path.exists(build.PROBE_LIB):
+        build.build()
+    src = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "wq_probe.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(wq_[a-z_]+)\s*\(", src)))
+    assert names == ["wq_probe_stream_read"]
+    P = ctypes.CDLL(build.PROBE_LIB)
+    for n in names:
+        assert hasattr(P, n), n
+    f = P.wq_probe_stream_read
+    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    # malformed arguments are refused before any launch
+    assert f(None, 4096, 64, 4, None, None) == 1
+    assert f(ctypes.c_void_p(4096), 4095, 64, 4, ctypes.c_void_p(64), None) == 1  # not a multiple of 16
+    assert f(ctypes.c_void_p(4096), 4096, 64, 3, ctypes.c_void_p(64), None) == 1  # loads in flight
+    assert f(ctypes.c_void_p(4096), 1 << 31, 1, 4, ctypes.c_void_p(64), None) == 2  # 2 GiB chunk

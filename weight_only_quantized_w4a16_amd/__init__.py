@@ -116,8 +116,56 @@ class PackedLayer:
     gate_up: bool = False                # repacked by wq_repack_gate_up (interleaved halves)
 
 
+def _need(cond: bool, what: str):
+    if not cond:
+        raise ValueError(what)
+
+
+def _check_tensor(t, name: str, dtypes, shape, device=None):
+    """t must be a contiguous tensor of one of `dtypes` with `shape` (and on `device`)."""
+    _need(isinstance(t, torch.Tensor), f"{name} must be a tensor")
+    _need(t.dtype in dtypes, f"{name} must have dtype {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
+    _need(tuple(t.shape) == tuple(shape), f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+    if device is not None:
+        _need(t.device == device, f"{name} must be on {device}, got {t.device}")
+
+
+def _check_cuda(t, name: str):
+    _need(t.device.type == "cuda", f"{name} must be a GPU tensor, got {t.device}")
+
+
+_FINE_ZG = {ZERO_F16_G8: 8, ZERO_F16_G16: 16, ZERO_F16_G32: 32}
+
+
 def _repack(fn: str, qweight, scales, zeros, mode, g_idx, K, N, bits, group_size, lut, stream) -> PackedLayer:
-    dev = qweight.device
+    # Every buffer is read by kernels through raw pointers: check shapes, dtypes,
+    # layout and device before anything is launched.
+    _need(bits in (2, 3, 4), f"bits must be 2, 3 or 4, got {bits}")
+    _need(K > 0 and N > 0 and (K * bits) % 32 == 0, f"bad shape K={K} N={N} bits={bits}")
+    _need(group_size == -1 or (group_size > 0 and K % group_size == 0), f"bad group_size {group_size}")
+    _need(mode in (SYM, ZERO_F16, ZERO_PACKED, LUT, ZERO_F16_G8, ZERO_F16_G16, ZERO_F16_G32), f"bad mode {mode}")
+    G = 1 if group_size == -1 else K // group_size
+    dev = qweight.device if isinstance(qweight, torch.Tensor) else None
+    _check_tensor(qweight, "qweight", (torch.int32,), (K * bits // 32, N), dev)
+    _check_tensor(scales, "scales", (torch.float16,), (G, N), dev)
+    if mode == ZERO_F16:
+        _check_tensor(zeros, "zeros", (torch.float16,), (G, N), dev)
+    elif mode == ZERO_PACKED:
+        _need((N * bits) % 32 == 0, "packed zero-points need N*bits % 32 == 0")
+        _check_tensor(zeros, "zeros", (torch.int32,), (G, N * bits // 32), dev)
+    elif mode in _FINE_ZG:
+        _need(K % _FINE_ZG[mode] == 0, "K must be a multiple of the zero-point group")
+        _check_tensor(zeros, "zeros", (torch.float16,), (K // _FINE_ZG[mode], N), dev)
+    else:
+        _need(zeros is None, "zeros must be None for this mode")
+    if mode == LUT:
+        _check_tensor(lut, "lut", (torch.float16,), (1 << bits,), dev)
+    else:
+        _need(lut is None, "lut is only used in table mode")
+    if g_idx is not None:
+        _need(len(g_idx) == K, f"g_idx must have K={K} entries")
+    _check_cuda(qweight, "qweight")
     nbytes = wq_packed_bytes(K, N, bits, group_size, mode)
     if nbytes == 0:
         raise WQError("wq_packed_bytes", 2)
@@ -154,6 +202,8 @@ def wq_repack_gate_up(qweight: torch.Tensor, scales: torch.Tensor, zeros: Option
 
 
 def wq_dequant_debug(layer: PackedLayer, dtype: torch.dtype, stream=None) -> torch.Tensor:
+    _dt(dtype)
+    _check_cuda(layer.packed, "layer.packed")
     w = torch.empty((layer.K, layer.N), dtype=dtype, device=layer.packed.device)
     rc = lib().wq_dequant_debug(_ptr(layer.packed), layer.mode, _ptr(layer.lut), _ptr(layer.perm),
                                 layer.K, layer.N, layer.bits, layer.group_size, _dt(dtype), _ptr(w),
@@ -164,17 +214,34 @@ def wq_dequant_debug(layer: PackedLayer, dtype: torch.dtype, stream=None) -> tor
 
 def _product(fn: str, x: torch.Tensor, layer: PackedLayer, out: Optional[torch.Tensor],
              ws: Optional[torch.Tensor], stream) -> torch.Tensor:
-    if x.dim() != 2 or x.shape[1] != layer.K or not x.is_contiguous():
-        raise ValueError("x must be a contiguous [M][K] tensor")
+    # The kernels take raw pointers: a short or misplaced buffer would be read
+    # or written out of bounds on the device, so everything is checked here,
+    # before the library is called.
+    _need(isinstance(x, torch.Tensor) and x.dim() == 2 and x.shape[1] == layer.K and x.is_contiguous(),
+          "x must be a contiguous [M][K] tensor")
+    _dt(x.dtype)
     M = x.shape[0]
     fused = "_gate_up" in fn
     if fused != layer.gate_up:
         raise ValueError(f"{fn} needs a layer repacked by "
                          f"{'wq_repack_gate_up' if fused else 'wq_repack'}")
-    if out is None:
-        out = torch.empty((M, layer.N // 2 if fused else layer.N), dtype=x.dtype, device=x.device)
+    ncols = layer.N // 2 if fused else layer.N
+    if out is not None:
+        _check_tensor(out, "out", (x.dtype,), (M, ncols), x.device)
     need = wq_workspace_bytes(M, layer.N, layer.K, layer.bits, layer.perm is not None)
-    if need and (ws is None or ws.numel() * ws.element_size() < need):
+    if ws is not None and need:
+        _need(isinstance(ws, torch.Tensor) and ws.is_contiguous() and ws.device == x.device,
+              "ws must be a contiguous tensor on the device of x")
+        _need(ws.numel() * ws.element_size() >= need, f"ws holds fewer than the {need} bytes this call needs")
+    _need(layer.packed.device == x.device, "x and the layer must be on the same device")
+    _check_cuda(x, "x")
+    if layer.lut is not None:
+        _need(layer.lut.device == x.device, "the layer's table must be on the device of x")
+    if layer.perm is not None:
+        _need(layer.perm.device == x.device and layer.perm.numel() == layer.K, "bad layer.perm")
+    if out is None:
+        out = torch.empty((M, ncols), dtype=x.dtype, device=x.device)
+    if need and ws is None:
         ws = torch.empty(need, dtype=torch.uint8, device=x.device)
     rc = getattr(lib(), fn)(_ptr(x), _dt(x.dtype), _ptr(layer.packed), layer.mode, _ptr(layer.lut),
                             _ptr(layer.perm), _ptr(out), M, layer.N, layer.K, layer.bits, layer.group_size,
@@ -209,10 +276,12 @@ def wq_hadamard(x: torch.Tensor, block: int, out: Optional[torch.Tensor] = None,
     if x.dim() != 2 or not x.is_contiguous():
         raise ValueError("x must be a contiguous [M][K] tensor")
     M, K = x.shape
+    _dt(x.dtype)
     if out is None:
         out = torch.empty_like(x)
-    elif out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor like x")
+    elif out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous() or out.device != x.device:
+        raise ValueError("out must be a contiguous tensor like x, on its device")
+    _check_cuda(x, "x")
     rc = lib().wq_hadamard(_ptr(x), _dt(x.dtype), _ptr(out), M, K, block, _stream(stream))
     _check("wq_hadamard", rc)
     return out

@@ -8,6 +8,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libwq.so")
+# measurement probe (streaming read), a library of its own outside the product ABI
+PROBE_LIB = os.path.join(HERE, "libwq_probe.so")
 # (source, object name, extra defines): the kernel files are compiled once
 # per (activation dtype, code width) so the instantiations build in parallel.
 SOURCES = [("wq_api.hip", "wq_api", []), ("wq_hadamard.hip", "wq_hadamard", [])]
@@ -42,13 +44,18 @@ def build(verbose: bool = False) -> str:
     jobs = min(len(SOURCES), int(os.environ.get("MAX_JOBS", str(os.cpu_count() or 8))), 16)
     with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+    _link(objs, LIB, verbose)
+    _link([_compile(("wq_probe.hip", "wq_probe", []), verbose)], PROBE_LIB, verbose)
+    return LIB
+
+
+def _link(objs, lib, verbose):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
 
 
 if __name__ == "__main__":

@@ -26,9 +26,10 @@ namespace {
 // LB = log2(block).  One thread per 8-element chunk; chunk c sits at position
 // c % (b / 8) of its block and, since waves start at multiples of 64 chunks,
 // that is lane % (b / 8) for every b <= 512.
+// x and y may be the same buffer (in-place rotation): each thread reads its
+// own 16 bytes before it writes them, so neither pointer is restrict.
 template <int DT, int LB>
-__global__ __launch_bounds__(256) void hadamard_kernel(const uint16_t* __restrict__ x, uint16_t* y, uint32_t chunks,
-                                                       float norm) {
+__global__ __launch_bounds__(256) void hadamard_kernel(const uint16_t* x, uint16_t* y, uint32_t chunks, float norm) {
   const uint32_t c = blockIdx.x * 256u + threadIdx.x;
   const int lane = threadIdx.x & 63;
   u32x4 raw = {0u, 0u, 0u, 0u};
