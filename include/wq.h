@@ -170,6 +170,28 @@ wq_status wq_gemm(const void* x, wq_dtype dt, const void* packed, wq_qmode mode,
                   int bits, int group_size, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * wq_gemm_noalloc -- wq_gemm without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  The scratch wq_gemm takes from
+ * `ws` (act-order permuted activations, K-split partial products) comes from
+ * one static device array per GPU of WQ_NOALLOC_SCRATCH_BYTES, which the
+ * library holds from its first use on that GPU until the process ends; this
+ * entry point allocates and frees nothing.
+ *   Arguments, limits and results as wq_gemm.  A call needing more scratch
+ *   than the array holds (wq_workspace_bytes(M, N, K, bits, perm != NULL) >
+ *   WQ_NOALLOC_SCRATCH_BYTES, e.g. act-order with M * K > 16 Mi) returns
+ *   WQ_ENOSPACE and launches nothing.
+ *   Every call on one GPU uses that GPU's one array: calls that overlap in
+ *   time on one GPU (different streams, or different host threads without
+ *   ordering) race on it and give undefined results.  Calls ordered on one
+ *   stream are safe; nothing in the array needs to start at zero.
+ */
+#define WQ_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+wq_status wq_gemm_noalloc(const void* x, wq_dtype dt, const void* packed, wq_qmode mode,
+                          const uint16_t* lut, const int32_t* perm, void* y, int M, int N, int K,
+                          int bits, int group_size, void* stream);
+
+/*
  * Activation-fused gate+up layer.  The Triton GPTQ page fuses the feed-forward
  * layers ("How It Works") without naming the activation; these entry points
  * read it as the gated SiLU of LLaMA-style blocks: for a weight W = [gate | up]

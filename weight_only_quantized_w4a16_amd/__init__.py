@@ -59,6 +59,8 @@ def lib() -> ctypes.CDLL:
             f = getattr(L, name)
             f.argtypes = [P, I, P, I, P, P, P, I, I, I, I, I, P, Z, P]
             f.restype = I
+        L.wq_gemm_noalloc.argtypes = [P, I, P, I, P, P, P, I, I, I, I, I, P]
+        L.wq_gemm_noalloc.restype = I
         L.wq_hadamard.argtypes = [P, I, P, I, I, I, P]
         L.wq_hadamard.restype = I
         if L.wq_layout_version() != LAYOUT_VERSION:
@@ -258,6 +260,27 @@ def wq_gemv(x: torch.Tensor, layer: PackedLayer, out=None, ws=None, stream=None)
 def wq_gemm(x: torch.Tensor, layer: PackedLayer, out=None, ws=None, stream=None) -> torch.Tensor:
     """y = x . dequant(W) for any M (prefill)."""
     return _product("wq_gemm", x, layer, out, ws, stream)
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # WQ_NOALLOC_SCRATCH_BYTES
+
+
+def wq_gemm_noalloc(x: torch.Tensor, layer: PackedLayer, out: torch.Tensor, stream=None) -> torch.Tensor:
+    """wq_gemm with the library's static scratch array instead of a workspace:
+    neither this call nor the library allocates (the caller passes `out`).
+    Calls that overlap in time on one GPU race on that array."""
+    _need(not layer.gate_up, "wq_gemm_noalloc takes a layer repacked by wq_repack")
+    _need(isinstance(x, torch.Tensor) and x.dim() == 2 and x.shape[1] == layer.K and x.is_contiguous(),
+          "x must be a contiguous [M][K] tensor")
+    _dt(x.dtype)
+    _check_tensor(out, "out", (x.dtype,), (x.shape[0], layer.N), x.device)
+    _need(layer.packed.device == x.device, "x and the layer must be on the same device")
+    _check_cuda(x, "x")
+    rc = lib().wq_gemm_noalloc(_ptr(x), _dt(x.dtype), _ptr(layer.packed), layer.mode, _ptr(layer.lut),
+                               _ptr(layer.perm), _ptr(out), x.shape[0], layer.N, layer.K, layer.bits,
+                               layer.group_size, _stream(stream))
+    _check("wq_gemm_noalloc", rc)
+    return out
 
 
 def wq_gemv_gate_up(x: torch.Tensor, layer: PackedLayer, out=None, ws=None, stream=None) -> torch.Tensor:

@@ -4,6 +4,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "wq_common.hpp"
@@ -392,6 +393,50 @@ static wq_status product(bool gemm, bool swiglu, const void* x, wq_dtype dt, con
   a.ksplit = ksplit;
   a.part = ksplit > 1 ? (void*)((uint8_t*)ws + perm_ws_bytes(M, K, perm != nullptr)) : nullptr;
   return launch_product(gemm, a);
+}
+
+// ---------------------------------------------------------------------------
+// Scratch for wq_gemm_noalloc: one static device array per GPU, the library's
+// only device memory of its own.  Its host-side name is not a device address;
+// the address comes from hipGetSymbolAddress, taken once per device (with
+// that device current) and kept.  The K-split partial products never exceed
+// 32 MiB (at most 512 slices x workgroups of 64 x 256 outputs, 4 bytes each);
+// the other 32 MiB hold the act-order permuted activations.
+// ---------------------------------------------------------------------------
+static constexpr size_t kScratchBytes = WQ_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+static constexpr int kMaxDevices = 64;
+static void* scratch_ptr[kMaxDevices];
+static std::mutex scratch_mu;
+
+// Device address of this GPU's scratch array (nullptr if it cannot be had).
+static void* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    scratch_ptr[dev] = p;
+  }
+  return scratch_ptr[dev];
+}
+
+wq_status wq_gemm_noalloc(const void* x, wq_dtype dt, const void* packed, wq_qmode mode, const uint16_t* lut,
+                          const int32_t* perm, void* y, int M, int N, int K, int bits, int group_size,
+                          void* stream) {
+  wq_status st = check_layer(K, N, bits, group_size, mode);
+  if (st != WQ_OK) return st;
+  if (M < 0) return WQ_EINVAL;
+  if (M == 0) return WQ_OK;
+  if (M > (1 << 24)) return WQ_EUNSUPPORTED;
+  // the same scratch wq_gemm would need, checked against the array's size
+  const size_t need = wq_workspace_bytes(M, N, K, bits, perm != nullptr);
+  if (need > kScratchBytes) return WQ_ENOSPACE;
+  void* ws = need ? device_scratch() : nullptr;
+  if (need && !ws) return WQ_EHIP;
+  return product(true, false, x, dt, packed, mode, lut, perm, y, M, N, K, bits, group_size, ws,
+                 need ? kScratchBytes : 0, stream);
 }
 
 wq_status wq_gemv(const void* x, wq_dtype dt, const void* packed, wq_qmode mode, const uint16_t* lut,
