@@ -16,9 +16,12 @@ replayed, so host-side launch cost does not starve the GPU; the eager
 
 Also reported:
   decode_other_m the same layer set at M = 4 and 16 (graph-replayed);
+  other_m1_layers  the single 4096 x 4096 layer and the largest (405B-width)
+                layer at M = 1, against HBM peak and the streaming-read ceiling;
   roofline      the dominant kernel (the gate+up GEMV, the largest layer)
-                against HBM bandwidth: its launches timed back to back over the
-                rotated copies between HIP events on its stream;
+                against HBM bandwidth: its launches back to back over the
+                rotated copies, captured in a HIP graph and timed between HIP
+                events on its stream;
   gemm          the prefill layer set at M = 2048 (symmetric int4, group -1 and
                 128) through wq_gemm, as TFLOP/s against dense fp16 MFMA peak
                 (each layer's launches graph-replayed; eager steps beside it);
@@ -149,9 +152,31 @@ class Dev:
         return out
 
 
+WARM_MS = 100.0  # GPU time spent on the measured work itself before any timing
+
+
+def warm_up(stream, replay, ms=WARM_MS):
+    """Run replay() (work on `stream`) until `ms` milliseconds of GPU time have
+    passed.  The GPU's clocks ramp up over tens of milliseconds after an idle
+    spell (host-side set-up, repacking): without this the first point timed
+    after a set-up measured up to 25 % slower than the same point timed later
+    in the same process."""
+    import torch
+    spent = 0.0
+    while spent < ms:
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        spent += max(e0.elapsed_time(e1), 0.01)
+
+
 def graph_time(stream, fn, n, replays=5):
     """fn(i) launches call i on `stream`; n calls captured in one HIP graph;
-    median over `replays` replays of the GPU time per call, in us."""
+    after warm_up(), the median over `replays` replays of the GPU time per
+    call, in us."""
     import statistics
 
     import torch
@@ -165,9 +190,11 @@ def graph_time(stream, fn, n, replays=5):
             for i in range(n):
                 fn(i)
     torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
-        g.replay()
-    torch.cuda.synchronize()
+
+    def replay():
+        with torch.cuda.stream(stream):
+            g.replay()
+    warm_up(stream, replay)
     ts = []
     for _ in range(replays):
         e0 = torch.cuda.Event(enable_timing=True)
@@ -480,6 +507,7 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    warm_up(stream, lambda: [step(i) for i in range(R)])
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
@@ -504,6 +532,7 @@ def main():
     for _ in range(max(1, args.warmup // R)):
         graph.replay()
     torch.cuda.synchronize()
+    warm_up(stream, graph.replay)
     e0.record(stream)
     for _ in range(replays):
         graph.replay()
@@ -528,18 +557,12 @@ def main():
     dom = int(np.argmax([L.weight_bytes() for L in layers]))
     Ld = layers[dom]
 
-    # dominant kernel (the largest layer): back-to-back launches over the
-    # rotated copies between two events on its stream -> average launch time
+    # dominant kernel (the largest layer): nd launches back to back over the
+    # rotated copies, captured in a HIP graph on stream s1 and replayed between
+    # two HIP events recorded on s1 -> average launch time (median of 5 replays)
     nd = max(args.steps, 4 * R)
-    for i in range(R):
-        wq.wq_gemv(xs[dom], packed[dom][i], out=ys[dom], stream=stream)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for i in range(nd):
-        wq.wq_gemv(xs[dom], packed[dom][i % R], out=ys[dom], stream=stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    dom_us = e0.elapsed_time(e1) / nd * 1e3
+    s1 = torch.cuda.Stream()
+    dom_us = graph_time(s1, lambda i: wq.wq_gemv(xs[dom], packed[dom][i % R], out=ys[dom], stream=s1), nd)
     alg_bytes = Ld.weight_bytes() + 2 * M * Ld.K + 2 * M * Ld.N
     achieved = alg_bytes / (dom_us * 1e-6) / 1e9
     khash = kernel_hash()
@@ -567,6 +590,7 @@ def main():
         torch.cuda.synchronize()
         gm.replay()
         torch.cuda.synchronize()
+        warm_up(stream, gm.replay)
         e0.record(stream)
         for _ in range(replays):
             gm.replay()
@@ -580,6 +604,39 @@ def main():
                   for L, t in zip(layers, kernel_us)}
     del packed, xs, ys
     torch.cuda.empty_cache()
+
+    # ---------------- the other M = 1 layers of the workloads ----------------
+    # The single 4096 x 4096 layer (c1: int4 symmetric, group 128, fp16) and
+    # the largest layer (c5: the 405B-width 16384 x 53248 act-order layer,
+    # bf16, packed zero-points, group 32), each through wq_gemv launched back
+    # to back over rotated copies in a HIP graph, against HBM peak and against
+    # the streaming-read ceiling of the same bytes (the probe kernel reading the
+    # same buffers under the same protocol).
+    extra_m1 = {}
+    s2 = torch.cuda.Stream()
+    for key, cid, lname in (("c1_4096x4096", 1, "layer"), ("c5_wide_16384x53248", 5, "wide")):
+        cx = wl.CONFIGS[cid]
+        Lx = cx.layer(lname)
+        wbx = Lx.weight_bytes()
+        Rx = max(2, -(-(1 << 30) // wbx))
+        cps = repack_copies(Lx, Rx)
+        tdt = torch.float16 if cx.dtype == wl.F16 else torch.bfloat16
+        xx = to_dev(cx.x(1, Lx.K), tdt)
+        yx = torch.empty((1, Lx.N), dtype=tdt, device=dev)
+        has_perm = cps[0].perm is not None
+        wsx = torch.empty(max(wq.wq_workspace_bytes(1, Lx.N, Lx.K, Lx.bits, has_perm), 16), dtype=torch.uint8,
+                          device=dev)
+        nx = Rx * max(1, -(-8 // Rx))
+        us = graph_time(s2, lambda i: wq.wq_gemv(xx, cps[i % Rx], out=yx, ws=wsx, stream=s2), nx, replays=7)
+        r_us, _, shape = read_ceiling(s2, [c.packed for c in cps], min(wbx, cps[0].packed.numel()), nx)
+        algx = wbx + 2 * Lx.K + 2 * Lx.N + (4 * Lx.K if has_perm else 0)
+        extra_m1[key] = {"config": cx.name, "layer": f"{lname} {Lx.K}x{Lx.N}", "M": 1, "bits": Lx.bits,
+                         "group": Lx.group_size, "us": round(us, 2), "weight_GBps": round(wbx / us / 1e3, 1),
+                         "algorithmic_bytes": algx, "frac_of_hbm_peak": round(algx / us / 1e3 / HBM_PEAK_GBS, 4),
+                         "read_ceiling_us": round(r_us, 2), "frac_of_read_ceiling": round(r_us / us, 3),
+                         "rotated_copies": Rx}
+        del cps, xx, yx, wsx
+        torch.cuda.empty_cache()
 
     # ---------------- prefill GEMM at M = 2048 ----------------
     gemm = None
@@ -623,6 +680,11 @@ def main():
                     gg.replay()
                 stream.wait_stream(cap)
                 torch.cuda.synchronize()
+
+                def gg_replay():
+                    with torch.cuda.stream(cap):
+                        gg.replay()
+                warm_up(cap, gg_replay)
                 ts = []
                 for _ in range(5):
                     with torch.cuda.stream(cap):
@@ -656,6 +718,7 @@ def main():
         I = Lg.N // 2
         Rg = max(2, -(-(1 << 30) // Lg.weight_bytes()))
         fused = {"layer": f"gate_up {Lg.K}x{Lg.N}", "rotated_copies": Rg}
+        sg = torch.cuda.Stream()
         plain = repack_copies(Lg, Rg)
         fpack = repack_copies(Lg, Rg, wq.wq_repack_gate_up)
         for Mf, fn, ffn in ((1, wq.wq_gemv, wq.wq_gemv_gate_up), (2048, wq.wq_gemm, wq.wq_gemm_gate_up)):
@@ -665,27 +728,19 @@ def main():
             n = max(4 * Rg, 40) if Mf == 1 else 2 * Rg
 
             def plain_call(i):
-                fn(xf, plain[i % Rg], out=yf, stream=stream)
+                fn(xf, plain[i % Rg], out=yf, stream=sg)
 
             def unfused_call(i):
-                fn(xf, plain[i % Rg], out=yf, stream=stream)
+                fn(xf, plain[i % Rg], out=yf, stream=sg)
                 torch.mul(torch.nn.functional.silu(yf[:, :I]), yf[:, I:], out=hf)
 
             def fused_call(i):
-                ffn(xf, fpack[i % Rg], out=hf, stream=stream)
+                ffn(xf, fpack[i % Rg], out=hf, stream=sg)
 
             res = {}
             for name, call in (("plain_us", plain_call), ("unfused_torch_silu_us", unfused_call),
                                ("fused_us", fused_call)):
-                for i in range(Rg):
-                    call(i)
-                torch.cuda.synchronize()
-                e0.record(stream)
-                for i in range(n):
-                    call(i)
-                e1.record(stream)
-                torch.cuda.synchronize()
-                res[name] = round(e0.elapsed_time(e1) / n * 1e3, 3)
+                res[name] = round(graph_time(sg, call, n), 3)
             if Mf == 1:
                 res["fused_weight_GBps"] = round(Lg.weight_bytes() / (res["fused_us"] * 1e-6) / 1e9, 1)
             else:
@@ -705,6 +760,7 @@ def main():
         Rq = max(2, -(-(1 << 30) // Lq.weight_bytes()))
         qp = repack_copies(Lq, Rq)
         had = {"layer": f"qkv {Lq.K}x{Lq.N}", "block": 128, "rotated_copies": Rq}
+        sh = torch.cuda.Stream()
         for Mh, fn in ((1, wq.wq_gemv), (2048, wq.wq_gemm)):
             xh = to_dev(cfg.x(Mh, Lq.K), torch.float16)
             xr = torch.empty_like(xh)
@@ -712,26 +768,18 @@ def main():
             n = max(4 * Rq, 40) if Mh == 1 else 2 * Rq
 
             def rot(i):
-                wq.wq_hadamard(xh, 128, out=xr, stream=stream)
+                wq.wq_hadamard(xh, 128, out=xr, stream=sh)
 
             def prod(i):
-                fn(xh, qp[i % Rq], out=yh, stream=stream)
+                fn(xh, qp[i % Rq], out=yh, stream=sh)
 
             def rot_prod(i):
-                wq.wq_hadamard(xh, 128, out=xr, stream=stream)
-                fn(xr, qp[i % Rq], out=yh, stream=stream)
+                wq.wq_hadamard(xh, 128, out=xr, stream=sh)
+                fn(xr, qp[i % Rq], out=yh, stream=sh)
 
             res = {}
             for name, call in (("rotate_us", rot), ("product_us", prod), ("rotate_then_product_us", rot_prod)):
-                for i in range(Rq):
-                    call(i)
-                torch.cuda.synchronize()
-                e0.record(stream)
-                for i in range(n):
-                    call(i)
-                e1.record(stream)
-                torch.cuda.synchronize()
-                res[name] = round(e0.elapsed_time(e1) / n * 1e3, 3)
+                res[name] = round(graph_time(sh, call, n), 3)
             res["rotate_GBps"] = round(4.0 * Mh * Lq.K / (res["rotate_us"] * 1e-6) / 1e9, 1)
             had[f"M{Mh}"] = res
             del xh, xr, yh
@@ -746,6 +794,7 @@ def main():
     fine = None
     if not args.no_fine:
         fine = {"bits": 2, "group_size": -1, "zero_group": 8, "layers": {}}
+        sfz = torch.cuda.Stream()
         for (name, K, N) in wl.LLAMA7B:
             Lf = wl.make_layer(K, N, 2, -1, wl.ZERO_F16_G8, 8100 + K + N, scale_range=(0.002, 0.01),
                                name=f"fine/{name}")
@@ -756,15 +805,7 @@ def main():
                 xf = to_dev(wl.make_x(Mf, K, wl.F16, 5), torch.float16)
                 yf = torch.empty((Mf, N), dtype=torch.float16, device=dev)
                 n = max(4 * Rf, 40) if Mf == 1 else Rf
-                for i in range(Rf):
-                    fn(xf, fp[i % Rf], out=yf, stream=stream)
-                torch.cuda.synchronize()
-                e0.record(stream)
-                for i in range(n):
-                    fn(xf, fp[i % Rf], out=yf, stream=stream)
-                e1.record(stream)
-                torch.cuda.synchronize()
-                us = e0.elapsed_time(e1) / n * 1e3
+                us = graph_time(sfz, lambda i: fn(xf, fp[i % Rf], out=yf, stream=sfz), n)
                 if Mf == 1:
                     res["M1_us"] = round(us, 3)
                     res["M1_weight_GBps"] = round(Lf.weight_bytes() / (us * 1e-6) / 1e9, 1)
@@ -818,7 +859,7 @@ def main():
                 x = torch.matmul(h, dw["down"])
             return x
 
-        def graph_time(fn):
+        def stack_time(fn):
             cap = torch.cuda.Stream()
             cap.wait_stream(stream)
             with torch.cuda.stream(cap):
@@ -834,6 +875,7 @@ def main():
             for _ in range(3):
                 g.replay()
             torch.cuda.synchronize()
+            warm_up(stream, g.replay)
             reps = max(5, args.stack_tokens)
             e0.record(stream)
             for _ in range(reps):
@@ -842,8 +884,8 @@ def main():
             torch.cuda.synchronize()
             return e0.elapsed_time(e1) / reps, reps
 
-        q_ms, reps = graph_time(lambda: st.step(x0, stream=torch.cuda.current_stream()))
-        d_ms, _ = graph_time(lambda: dense_step(x0))
+        q_ms, reps = stack_time(lambda: st.step(x0, stream=torch.cuda.current_stream()))
+        d_ms, _ = stack_time(lambda: dense_step(x0))
         dbytes = sum(sum(t.numel() * 2 for t in dw.values()) for dw in dense)
         stack = {"layers": nl, "M": Ms, "tokens_timed": reps, "setup_s": round(setup_s, 1),
                  "quantized": {"ms_per_token": round(q_ms, 4), "tokens_per_s": round(1e3 / q_ms, 1),
@@ -900,7 +942,8 @@ def main():
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "eager": {"ms_per_step": round(eager_ms_per_step, 5),
                   "value": round(set_bytes / (eager_ms_per_step * 1e-3) / 1e9, 1)},
-        "roofline": roofline, "per_kernel": per_kernel, "decode_other_m": decode_m, "gemm_m2048": gemm,
+        "roofline": roofline, "per_kernel": per_kernel, "decode_other_m": decode_m, "other_m1_layers": extra_m1,
+        "gemm_m2048": gemm,
         "fused_gate_up": fused, "hadamard": had, "fine_zero_groups": fine, "layer_stack": stack, "cpu_baseline": cpu,
         "kernel_sources_sha256_16": khash,
     }

@@ -87,7 +87,7 @@ typedef enum {
 
 /* Version of the repacked layout; a stored repacked buffer from another
  * version must be repacked again. */
-#define WQ_LAYOUT_VERSION 2
+#define WQ_LAYOUT_VERSION 3
 int wq_layout_version(void);
 
 const char* wq_status_str(wq_status s);

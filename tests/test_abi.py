@@ -40,7 +40,7 @@ def test_library_exports_every_declared_function(L):
 
 
 def test_status_strings_and_version(L):
-    assert L.wq_layout_version() == 2
+    assert L.wq_layout_version() == 3
     for s in range(5):
         assert L.wq_status_str(s)
 

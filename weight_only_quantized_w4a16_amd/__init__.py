@@ -18,7 +18,7 @@ import torch
 SYM, ZERO_F16, ZERO_PACKED, LUT = 0, 1, 2, 3
 ZERO_F16_G8, ZERO_F16_G16, ZERO_F16_G32 = 4, 5, 6  # fp16 zero-points per 8 / 16 / 32 rows
 F16, BF16 = 0, 1
-LAYOUT_VERSION = 2
+LAYOUT_VERSION = 3
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libwq.so")
@@ -118,23 +118,30 @@ class PackedLayer:
     gate_up: bool = False                # repacked by wq_repack_gate_up (interleaved halves)
 
 
-def _need(cond: bool, what: str):
+def _need(cond: bool, what):
+    """Raise ValueError(what) unless cond; `what` may be a callable that builds
+    the message (so a passing check costs no string formatting)."""
     if not cond:
-        raise ValueError(what)
+        raise ValueError(what() if callable(what) else what)
 
 
 def _check_tensor(t, name: str, dtypes, shape, device=None):
     """t must be a contiguous tensor of one of `dtypes` with `shape` (and on `device`)."""
-    _need(isinstance(t, torch.Tensor), f"{name} must be a tensor")
-    _need(t.dtype in dtypes, f"{name} must have dtype {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
-    _need(tuple(t.shape) == tuple(shape), f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
-    _need(t.is_contiguous(), f"{name} must be contiguous")
-    if device is not None:
-        _need(t.device == device, f"{name} must be on {device}, got {t.device}")
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} must have dtype {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
+    if t.shape != shape:
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
 
 
 def _check_cuda(t, name: str):
-    _need(t.device.type == "cuda", f"{name} must be a GPU tensor, got {t.device}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor, got {t.device}")
 
 
 _FINE_ZG = {ZERO_F16_G8: 8, ZERO_F16_G16: 16, ZERO_F16_G32: 32}
@@ -143,10 +150,11 @@ _FINE_ZG = {ZERO_F16_G8: 8, ZERO_F16_G16: 16, ZERO_F16_G32: 32}
 def _repack(fn: str, qweight, scales, zeros, mode, g_idx, K, N, bits, group_size, lut, stream) -> PackedLayer:
     # Every buffer is read by kernels through raw pointers: check shapes, dtypes,
     # layout and device before anything is launched.
-    _need(bits in (2, 3, 4), f"bits must be 2, 3 or 4, got {bits}")
-    _need(K > 0 and N > 0 and (K * bits) % 32 == 0, f"bad shape K={K} N={N} bits={bits}")
-    _need(group_size == -1 or (group_size > 0 and K % group_size == 0), f"bad group_size {group_size}")
-    _need(mode in (SYM, ZERO_F16, ZERO_PACKED, LUT, ZERO_F16_G8, ZERO_F16_G16, ZERO_F16_G32), f"bad mode {mode}")
+    _need(bits in (2, 3, 4), lambda: f"bits must be 2, 3 or 4, got {bits}")
+    _need(K > 0 and N > 0 and (K * bits) % 32 == 0, lambda: f"bad shape K={K} N={N} bits={bits}")
+    _need(group_size == -1 or (group_size > 0 and K % group_size == 0), lambda: f"bad group_size {group_size}")
+    _need(mode in (SYM, ZERO_F16, ZERO_PACKED, LUT, ZERO_F16_G8, ZERO_F16_G16, ZERO_F16_G32),
+          lambda: f"bad mode {mode}")
     G = 1 if group_size == -1 else K // group_size
     dev = qweight.device if isinstance(qweight, torch.Tensor) else None
     _check_tensor(qweight, "qweight", (torch.int32,), (K * bits // 32, N), dev)
@@ -166,7 +174,7 @@ def _repack(fn: str, qweight, scales, zeros, mode, g_idx, K, N, bits, group_size
     else:
         _need(lut is None, "lut is only used in table mode")
     if g_idx is not None:
-        _need(len(g_idx) == K, f"g_idx must have K={K} entries")
+        _need(len(g_idx) == K, lambda: f"g_idx must have K={K} entries")
     _check_cuda(qweight, "qweight")
     nbytes = wq_packed_bytes(K, N, bits, group_size, mode)
     if nbytes == 0:
@@ -234,7 +242,7 @@ def _product(fn: str, x: torch.Tensor, layer: PackedLayer, out: Optional[torch.T
     if ws is not None and need:
         _need(isinstance(ws, torch.Tensor) and ws.is_contiguous() and ws.device == x.device,
               "ws must be a contiguous tensor on the device of x")
-        _need(ws.numel() * ws.element_size() >= need, f"ws holds fewer than the {need} bytes this call needs")
+        _need(ws.numel() * ws.element_size() >= need, lambda: f"ws holds fewer than the {need} bytes this call needs")
     _need(layer.packed.device == x.device, "x and the layer must be on the same device")
     _check_cuda(x, "x")
     if layer.lut is not None:

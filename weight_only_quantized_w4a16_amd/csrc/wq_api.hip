@@ -71,7 +71,7 @@ __global__ void repack_codes_kernel(const uint32_t* __restrict__ qw, const int32
   uint32_t w[4] = {0u, 0u, 0u, 0u};
   for (int kb = 0; kb < KB; ++kb) {
     for (int e = 0; e < 8; ++e) {
-      const int row = kt * KT + 32 * kb + 8 * h + e;
+      const int row = kt * KT + tile_row(kb, h, e);
       const int k = perm ? perm[row] : row;
       place_code<BITS, TABLE_LAYOUT>(w, kb, e, canonical_code<BITS>(qw, N, n, k));
     }
@@ -115,20 +115,18 @@ __global__ void repack_zeros_packed_kernel(const uint32_t* __restrict__ zp, int 
   dst[i] = word;
 }
 
-// Fine zero-points: fp16 [K / zg][N] -> [N/16][K/128][16][HC][4] (layout in
+// Fine zero-points: fp16 [K / zg][N] -> [N/16][K/128][16][128/zg] (layout in
 // wq_layout.hpp).  One thread per entry.
 __global__ void repack_zeros_fine_kernel(const uint16_t* __restrict__ zeros, int N, int K, int zg, int ntiles,
                                          int gate_up, uint16_t* __restrict__ dst) {
-  const int hcs = 32 / zg;  // row classes per k-block
-  const size_t total = (size_t)ntiles * (K / 128) * 16 * hcs * 4;
+  const int per = fine_per_unit(zg);  // entries per column and unit
+  const size_t total = (size_t)ntiles * (K / 128) * 16 * per;
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= total) return;
-  const int kb = (int)(i % 4), hc = (int)((i / 4) % hcs), c = (int)((i / (4 * hcs)) % 16);
-  const size_t rest = i / (64 * hcs);
+  const int e = (int)(i % per), c = (int)((i / per) % 16);
+  const size_t rest = i / (16 * per);
   const int u = (int)(rest % (K / 128)), nt = (int)(rest / (K / 128));
-  const int h0 = hc * 4 / hcs;  // first lane row block of the class
-  const int row = 128 * u + 32 * kb + 8 * h0;
-  dst[i] = zeros[(size_t)(row / zg) * N + source_tile(nt, ntiles, gate_up) * 16 + c];
+  dst[i] = zeros[(size_t)(u * per + e) * N + source_tile(nt, ntiles, gate_up) * 16 + c];
 }
 
 // ---------------------------------------------------------------------------
@@ -160,7 +158,7 @@ __global__ __launch_bounds__(64) void dequant_debug_kernel(const uint8_t* __rest
   const int n = nt * 16 + c;
   sfor<KB>([&](auto kbc) {
     constexpr int kb = decltype(kbc)::value;
-    const int row0 = kt * KT + 32 * kb + 8 * h;
+    const int row0 = kt * KT + tile_row(kb, h, 0);
     const int unit = row0 / 128;
     const int rec = meta_record(unit, L.gsz);
     const int j = L.gpu > 1 ? (row0 % 128) / L.gsz : 0;  // group inside the record
@@ -168,8 +166,8 @@ __global__ __launch_bounds__(64) void dequant_debug_kernel(const uint8_t* __rest
     float sv, zv;
     if (MODE == ZFINE) {
       sv = f16_to_f32(((const uint16_t*)S)[ri]);
-      const int zg = fine_zero_group(L.mode), hcs = 32 / zg;
-      const size_t zi = ((((size_t)nt * (L.K / 128) + unit) * 16 + c) * hcs + h * hcs / 4) * 4 + (row0 % 128) / 32;
+      const int zg = fine_zero_group(L.mode);
+      const size_t zi = (((size_t)nt * (L.K / 128) + unit) * 16 + c) * fine_per_unit(zg) + (row0 % 128) / zg;
       zv = f16_to_f32(((const uint16_t*)Z)[zi]);
     } else if (MODE == ZERO_F16) {
       const uint32_t w2 = ((const uint32_t*)S)[ri];

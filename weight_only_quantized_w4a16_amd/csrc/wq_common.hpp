@@ -73,6 +73,10 @@ struct ProductArgs {
   hipStream_t stream;
   int ksplit = 1;           // GEMM only: K split over this many workgroups
   void* part = nullptr;     // ksplit > 1: fp32 workspace [ksplit][M][N]
+  // GEMV launch shape for measurements of the shape choice itself: waves per
+  // workgroup and prefetch depth (0: the library's own choice, which every
+  // entry point uses)
+  int waves = 0, pf = 0;
 };
 #define WQ_CAT2(a, b) a##b
 #define WQ_CAT(a, b) WQ_CAT2(a, b)

@@ -318,37 +318,25 @@ __device__ inline u32x4 table_frag(const uint32_t* w, const uint32_t* tab) {
 
 // Fill an LDS pair table: entry idx = value[lo] | value[hi] << 16 with
 // lo = idx & (2^BITS - 1), hi = idx >> BITS, replicated over COPIES columns.
-// AS_BF16: store RN_bf16(T) instead of the fp16 T.
+// AS_BF16: store RN_bf16(T) instead of the fp16 T.  Each thread writes 16
+// bytes (four copies of one entry) per step; consecutive threads write
+// consecutive 16-byte chunks, so the writes of a wave hit every bank once.
+// `table` must be 16-byte aligned.
 template <int BITS, bool AS_BF16, int COPIES = 32>
 __device__ inline void fill_pair_table(uint32_t* table, const uint16_t* lut, int tid, int nthreads) {
+  static_assert(COPIES % 4 == 0, "copies come in 16-byte chunks");
   constexpr int n = 1 << (2 * BITS);
   constexpr int mask = (1 << BITS) - 1;
-  for (int i = tid; i < n * COPIES; i += nthreads) {
-    const int idx = i / COPIES;
+  constexpr int CPE = COPIES / 4;  // chunks per entry
+  for (int i = tid; i < n * CPE; i += nthreads) {
+    const int idx = i / CPE;
     uint16_t lo = lut[idx & mask], hi = lut[idx >> BITS];
     if (AS_BF16) {
       lo = f32_to_bf16(f16_to_f32(lo));
       hi = f32_to_bf16(f16_to_f32(hi));
     }
-    table[i] = (uint32_t)lo | ((uint32_t)hi << 16);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Code of element E (0..7) of k-block KB, for the generic exact path.
-// ---------------------------------------------------------------------------
-template <int BITS, bool TABLE_LAYOUT, int KB, int E>
-__device__ inline uint32_t code_at(const uint32_t* w) {
-  if constexpr (BITS == 4) {
-    constexpr int nib = TABLE_LAYOUT ? E : (E % 2) * 4 + E / 2;
-    return (w[KB] >> (4 * nib)) & 0xFu;
-  } else if constexpr (BITS == 2) {
-    constexpr int i = 4 * (KB % 2) + E / 2;
-    constexpr int pos = TABLE_LAYOUT ? 4 * i + 2 * (E % 2) : 16 * (E % 2) + 2 * i;
-    return (w[KB / 2] >> pos) & 0x3u;
-  } else {
-    const uint32_t f = pair6<(4 * KB + E / 2) % 16>(w);
-    return (E % 2) ? (f >> 3) : (f & 7u);
+    const uint32_t v = (uint32_t)lo | ((uint32_t)hi << 16);
+    *(u32x4*)(table + 4 * i) = u32x4{v, v, v, v};
   }
 }
 
@@ -384,7 +372,8 @@ __device__ inline u32x4 exact_frag(const uint32_t* w, const ExactParams& p, cons
       const h2 v = as_h2(t[q]);
       r[q] = pack2<DT>(__builtin_fmaf((float)v[0], p.s, k.nzero), __builtin_fmaf((float)v[1], p.s, k.nzero));
     }
-  } else if constexpr (DT == BF16) {
+  } else {
+    // (bf16 activations, and fp16 activations with stored zero-points.)
     // Codes decoded as fp16 (1024 + q) pairs, widened inside v_fma_mix:
     //   integer zero-points: s * (1024 + q) - s * (1024 + z) = s * (q - z),
     //     every term exact in fp32 (at most 22 significant bits);
@@ -417,15 +406,6 @@ __device__ inline u32x4 exact_frag(const uint32_t* w, const ExactParams& p, cons
       }
       r[q] = pack2<DT>(lo, hi);
     }
-  } else {
-    constexpr bool TL = false;
-    const float c[8] = {(float)code_at<BITS, TL, KB, 0>(w), (float)code_at<BITS, TL, KB, 1>(w),
-                        (float)code_at<BITS, TL, KB, 2>(w), (float)code_at<BITS, TL, KB, 3>(w),
-                        (float)code_at<BITS, TL, KB, 4>(w), (float)code_at<BITS, TL, KB, 5>(w),
-                        (float)code_at<BITS, TL, KB, 6>(w), (float)code_at<BITS, TL, KB, 7>(w)};
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      r[q] = pack2<DT>(__builtin_fmaf(c[2 * q], p.s, -p.sz), __builtin_fmaf(c[2 * q + 1], p.s, -p.sz));
   }
   return r;
 }

@@ -41,7 +41,6 @@ struct GemmArgs {
   uint32_t codes_bytes, s_bytes, z_bytes;
   int M, N, K, nrec, upr, ktiles, ntiles, mtiles, ntiles_wg;  // upr: 128-row units per metadata record
   int swiglu;             // fused gate+up layer: y [M][N/2] = SiLU(gate) * up
-  int zg;                 // rows per fine zero-point group (fine mode only)
   int ksplit, ktps;       // K split over ksplit workgroups of ktps k-tiles (1: no split)
   float* part;            // ksplit > 1: fp32 partial products [ksplit][M][N]
 };
@@ -57,14 +56,15 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
   constexpr int UPT = KT / 128;
   constexpr int WPL = BITS == 3 ? 3 : 4;
   constexpr int MT = BM / 16;         // 16-row subtiles per wave (a wave covers all BM rows)
-  constexpr int KBPG = 4 / GPU;
   constexpr bool TABLE = MODE == LUT;
   constexpr bool Z16 = MODE == ZERO_F16;
-  constexpr int REC = (Z16 ? 4 : 2) * GPU;   // scale record bytes per column
-  constexpr int SW = REC < 4 ? 1 : REC / 4;  // words per scale record
+  constexpr bool FINE = MODE >= ZFINE;       // fp16 zero-points per ZG rows (MODE is the ABI mode)
+  constexpr int ZG = fine_zero_group(MODE);
+  constexpr int ZPL = FINE ? fine_per_lane(ZG) : 0;  // fine zero-points of a lane per unit
+  constexpr int SB = Z16 ? 4 : 2;            // bytes of a lane's scale (+ zero) entry
+  constexpr int REC = SB * GPU;              // scale record bytes per column
   constexpr int ZREC = 4 * GPU;              // packed-zero record bytes per column half
-  constexpr bool FINE = MODE == ZFINE;       // fp16 zero-point per k-block row block
-  constexpr int ZW = MODE == ZERO_PACKED ? GPU : FINE ? 2 : 1;
+  constexpr int ZW = FINE ? (ZPL + 1) / 2 : 1;  // words of a lane's zero entry
   constexpr int AW = BM / 16;         // 1-KiB activation loads per wave per unit
 
   // Table columns: 32 (one per lane of a half-wave), 16 for 4-bit tables in
@@ -74,7 +74,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
   // one-shift nibble decode (bf16) except in 128 x 256 tiles, where its two
   // extra registers per column tile would spill
   constexpr bool SPLIT4 = !(BM == 128 && NT == 4);
-  __shared__ uint32_t table[TABLE ? (COPIES << (2 * BITS)) : 1];
+  __shared__ __attribute__((aligned(16))) uint32_t table[TABLE ? (COPIES << (2 * BITS)) : 4];
   // Two stages of the BM x 128 activation tile, 16-byte chunks, row r at
   // chunk (c ^ (r % 16)).  Separate arrays so each stage's reads and loads are
   // distinct objects.
@@ -101,10 +101,12 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
   const rsrc_t rc = make_rsrc(a.codes, a.codes_bytes);
   const rsrc_t rs = make_rsrc(a.S, a.s_bytes);
   const rsrc_t rz = make_rsrc(MODE == ZERO_PACKED || FINE ? a.Z : a.S, MODE == ZERO_PACKED || FINE ? a.z_bytes : 0u);
-  // fine zero records: 8 * hcs bytes per column and 128-row unit, this lane's row class at 8 hc
-  const int hcs = FINE ? 32 / a.zg : 1;
-  const uint32_t zf_rec = 8u * hcs;
-  const uint32_t zf_lane = (uint32_t)c * zf_rec + 8u * ((h * hcs) >> 2);
+  // metadata: the lane's own group of each unit (the tile row map gives lane
+  // half h rows 32 h .. 32 h + 31 of every unit)
+  const int jg = lane_group(h, GPU);
+  const uint32_t s_lane = (uint32_t)(c * REC + jg * SB);
+  const uint32_t zp_lane = (uint32_t)((c >> 3) * ZREC + 4 * jg);
+  const uint32_t zf_lane = FINE ? (uint32_t)((c * fine_per_unit(ZG > 0 ? ZG : 32) + h * ZPL) * 2) : 0u;
 
   if constexpr (TABLE) fill_pair_table<BITS, false, COPIES>(table, a.lut, tid, 256);
   const uint32_t* tab = table + (lane % COPIES);
@@ -135,13 +137,14 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
     const int nt = min(nt0 + t, a.ntiles - 1);
     b_voff[t] = (uint32_t)(nt * a.ktiles * 64 + lane) * WPL * 4;
     s_soff_t[t] = (uint32_t)(nt * a.nrec) * 16 * REC;
-    z_soff_t[t] = FINE ? (uint32_t)(nt * a.ktiles * UPT) * 16u * zf_rec : (uint32_t)(nt * a.nrec) * 2 * ZREC;
+    z_soff_t[t] = FINE ? (uint32_t)(nt * a.ktiles * UPT) * 32u * fine_per_unit(ZG > 0 ? ZG : 32)
+                       : (uint32_t)(nt * a.nrec) * 2 * ZREC;
   }
   // Weight registers of one tile.
   struct BSet {
     uint32_t w[NT][WPL];
-    uint32_t s[UPT][NT][SW];
-    uint32_t z[UPT][NT][ZW];
+    uint32_t s[UPT][NT];       // the lane's scale (with its fp16 zero-point when Z16)
+    uint32_t z[UPT][NT][ZW];   // the lane's packed or fine zero-points
   };
   // loads issued by one b_load (codes, scale records, packed-zero records)
   constexpr int NBL = NT * (1 + (EPI_SCALE ? 0 : UPT) + (MODE == ZERO_PACKED || FINE ? UPT : 0));
@@ -170,11 +173,12 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
         const uint32_t rec = (uint32_t)((ktc * UPT + u) / a.upr);
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-          load_record<REC>(rs, (uint32_t)c * REC + oob, s_soff_t[t] + rec * 16 * REC, bs.s[u][t]);
+          load_record<SB>(rs, s_lane + oob, s_soff_t[t] + rec * 16 * REC, &bs.s[u][t]);
           if constexpr (MODE == ZERO_PACKED)
-            load_record<ZREC>(rz, (uint32_t)(c >> 3) * ZREC + oob, z_soff_t[t] + rec * 2 * ZREC, bs.z[u][t]);
+            load_record<4>(rz, zp_lane + oob, z_soff_t[t] + rec * 2 * ZREC, bs.z[u][t]);
           if constexpr (FINE)
-            load_record<8>(rz, zf_lane + oob, z_soff_t[t] + (uint32_t)(ktc * UPT + u) * 16u * zf_rec, bs.z[u][t]);
+            load_record<2 * ZPL>(rz, zf_lane + oob,
+                                 z_soff_t[t] + (uint32_t)(ktc * UPT + u) * 32u * fine_per_unit(ZG), bs.z[u][t]);
         }
       }
     }
@@ -186,10 +190,12 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[i][t] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // A fragment (activation rows 16 i .. 16 i + 15, k-block kbu) from stage As.
+  // A fragment (activation rows 16 i .. 16 i + 15, k-block kbu) from stage As:
+  // lane half h takes unit rows 32 h + 8 kbu .. + 7 (the tile row map), i.e.
+  // 16-byte chunk 4 h + kbu of the row.
   auto a_frag = [&](const u32x4* As, int kbu, int i) {
     const int r = 16 * i + c;
-    return As[r * 16 + ((4 * kbu + h) ^ (r & 15))];
+    return As[r * 16 + ((kbu + 4 * h) ^ (r & 15))];
   };
   // One 128-row unit of K from stage `As`: 4 k-blocks of MT x NT MFMAs, taken
   // as pairs of row subtiles.  With 128-row tiles the A fragments of the next
@@ -198,7 +204,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
   // extra registers would cost a wave per SIMD, so the reads stay next to
   // their MFMAs.
   constexpr bool LOOKAHEAD = BM == 128;
-  auto compute_unit = [&](const u32x4* As, const uint32_t (&cw)[NT][WPL], const uint32_t (&cs)[NT][SW],
+  auto compute_unit = [&](const u32x4* As, const uint32_t (&cw)[NT][WPL], const uint32_t (&cs)[NT],
                           const uint32_t (&cz)[NT][ZW], auto uc) {
     constexpr int u = decltype(uc)::value;
     constexpr int PAIRS = MT / 2;       // row-subtile pairs per k-block
@@ -214,15 +220,14 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
       constexpr int step = decltype(sc)::value;
       constexpr int kbu = step / PAIRS, ip = step % PAIRS;  // k-block inside the unit, pair
       constexpr int kb = 4 * u + kbu;                         // k-block inside the tile
-      constexpr int gi = kbu / KBPG;                          // group inside the unit
       if constexpr (ip == 0) {
-        if constexpr (!EPI_SCALE && kbu % KBPG == 0) {
+        if constexpr (!EPI_SCALE && kbu == 0) {  // the lane's group of this unit
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
-            const float sv = rec_scale<Z16>(cs[t], gi);
+            const float sv = f16_to_f32((uint16_t)(cs[t] & 0xFFFFu));
             float z;
-            if constexpr (MODE == ZERO_F16) z = rec_zero16(cs[t], gi);
-            else if constexpr (MODE == ZERO_PACKED) z = rec_zero_packed(cz[t], gi, c);
+            if constexpr (MODE == ZERO_F16) z = f16_to_f32((uint16_t)(cs[t] >> 16));
+            else if constexpr (MODE == ZERO_PACKED) z = (float)((cz[t][0] >> (4 * (c & 7))) & 0xFu);
             else z = (float)(1 << (BITS - 1));
             prm[t].s = sv;
             prm[t].s_h = h2s(sv);
@@ -235,12 +240,13 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
           if constexpr (EPI_SCALE) {
             bf[t] = offset_frag<BITS, DT, kb>(cw[t], dk);
           } else if constexpr (FINE) {
-            // the k-block's own zero-point
+            // the k-block's own zero-point: entry kbu * ZPL / 4 of the lane's
+            constexpr int zi = kbu * ZPL / 4;
             ExactParams pk = prm[t];
-            const float zk = f16_to_f32((uint16_t)fine_zero_bits(cz[t], kbu));
+            const float zk = f16_to_f32((uint16_t)((cz[t][zi >> 1] >> (16 * (zi & 1))) & 0xFFFFu));
             pk.sz = pk.s * zk;
             pk.nz_h = h2s(-zk);
-            bf[t] = product_frag<BITS, DT, MODE, kb, COPIES, SPLIT4>(cw[t], pk, tab, dk);
+            bf[t] = product_frag<BITS, DT, ZFINE, kb, COPIES, SPLIT4>(cw[t], pk, tab, dk);
           } else {
             bf[t] = product_frag<BITS, DT, MODE, kb, COPIES, SPLIT4>(cw[t], prm[t], tab, dk);
           }
@@ -531,16 +537,15 @@ wq_status WQ_CAT(launch_gemm_, WQ_VARIANT)(const ProductArgs& p) {
   g.ktiles = L.ktiles; g.ntiles = L.ntiles;
   g.mtiles = 0; g.ntiles_wg = 0;
   g.swiglu = p.swiglu;
-  g.zg = fine_zero_group(p.mode);
   g.ksplit = p.ksplit;
   g.part = (float*)p.part;
   g.ktps = L.ktiles;
   const int gpu = L.gsz >= 128 ? 1 : 128 / L.gsz;
   const bool epi = L.G == 1 && p.mode == SYM && D == F16;
   wq_status st = WQ_EINVAL;
-  sfor<5>([&](auto mi) {
+  sfor<7>([&](auto mi) {  // the ABI mode itself: fine zero-points keep their group
     constexpr int MODE = decltype(mi)::value;
-    if (MODE != kernel_mode(p.mode)) return;
+    if (MODE != p.mode) return;
     if (gpu == 1) {
       if (epi) { if constexpr (MODE == SYM && D == F16) st = run_gemm<D, B, MODE, 1, true>(g, p.stream); }
       else st = run_gemm<D, B, MODE, 1, false>(g, p.stream);

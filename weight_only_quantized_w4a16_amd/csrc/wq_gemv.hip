@@ -48,30 +48,41 @@ struct GemvArgs {
   uint32_t codes_bytes, s_bytes, z_bytes;
   int M, N, K, nrec, upr, ktiles, waves, kt_per_wave;  // upr: 128-row units per metadata record
   int ldy;                // row stride of y (N, or N / 2 for a fused gate+up layer)
-  int zg;                 // rows per fine zero-point group (8, 16, 32; fine mode only)
+  int force_waves, force_pf;  // launch-shape overrides (0: automatic)
 };
 
-// Decode k-block KB of a tile into a B operand.  fp16 activations: the
-// biased code bias + q (scale and zero-point follow the MFMA), the table
-// value T[q], or, for fine zero-points, RN(q - z) with zbits the k-block's
-// zero-point (11 bits, the scale follows the MFMA).  bf16 activations: the
-// dequantised weight RN_bf16(s * (q - z)) or RN_bf16(s * T[q]) itself (z the
-// group's zero-point, or the fine one in zbits) and no scale follows: a bf16
-// operand keeps only 8 bits, so applying the scale after the MFMA would
+// Whether the product multiplies the dequantised weights themselves (the
+// exact decode, no scale after the MFMA).  With bf16 activations always: a
+// bf16 operand keeps only 8 bits, so applying the scale after the MFMA would
 // multiply other weights than the rounded ones the product is defined on --
 // one further bf16 rounding per weight, which with the bf16 rounding of the
-// output measured outside the tolerance on a 2048-row layer.
-template <int BITS, int DT, int MODE, int KB>
+// output measured outside the tolerance on a 2048-row layer.  With fp16
+// activations when a unit holds more than one scale group: the four quarters
+// of every MFMA k-block then belong to different groups (the tile row map),
+// so no single scale can follow the MFMA.
+template <int DT, int GPU>
+constexpr bool gemv_scaled() { return DT == BF16 || GPU > 1; }
+
+// Decode k-block KB of a tile into a B operand.  SCALED: the dequantised
+// weight RN(s * (q - z)) or RN(s * T[q]) in the activation dtype, exactly the
+// bits of the debug dump (zbits: the k-block's fine zero-point).  Otherwise
+// (fp16, one group per unit): the biased code bias + q (scale and zero-point
+// follow the MFMA), the table value T[q], or, for fine zero-points, RN(q - z)
+// (11 bits; the scale follows the MFMA).
+template <int BITS, int DT, int MODE, int KB, bool SCALED>
 __device__ inline u32x4 decode_frag(const uint32_t* w, const uint32_t* tab, const DecodeConsts& k, uint32_t zbits,
-                                    float s, float z) {
-  if constexpr (DT == BF16) {
-    ExactParams p;
-    p.s = s;
-    p.sz = MODE == LUT ? 0.0f : s * (MODE == ZFINE ? f16_to_f32((uint16_t)zbits) : z);
-    return exact_frag<BITS, DT, MODE, KB>(w, p, tab, k);
+                                    const ExactParams& p) {
+  if constexpr (SCALED) {
+    if constexpr (MODE >= ZFINE) {
+      ExactParams q = p;
+      q.sz = p.s * f16_to_f32((uint16_t)zbits);
+      return exact_frag<BITS, DT, ZFINE, KB>(w, q, tab, k);
+    } else {
+      return exact_frag<BITS, DT, MODE, KB>(w, p, tab, k);
+    }
   } else if constexpr (MODE == LUT) {
     return table_frag<BITS, KB>(w, tab);
-  } else if constexpr (MODE == ZFINE) {
+  } else if constexpr (MODE >= ZFINE) {
     return fine_frag<BITS, DT, KB>(w, zbits, k);
   } else {
     return biased_frag<BITS, KB>(w, k);
@@ -101,6 +112,7 @@ constexpr int gemv_wave_lds() {
   return STAGE && red < 4096 ? 4096 : red;
 }
 
+// MODE is the C ABI mode (fine zero-points keep their group: 4, 5, 6).
 // SWIGLU: the layer is a fused gate+up layer repacked with interleaved column
 // tiles (gate, up, gate, up, ...).  Workgroup p owns output tile p: its even
 // waves stream gate tile 2p, its odd waves up tile 2p + 1 (TN = 1, each pair
@@ -117,20 +129,20 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU, MR>() ? 512 : 1024)
   constexpr int UPT = KT / 128;                 // 128-row units per tile
   constexpr int WPL = BITS == 3 ? 3 : 4;
   constexpr int NXA = PK == 4 ? UPT : PK == 8 ? 2 * UPT : 4 * UPT;  // activation loads per tile
-  constexpr int KBPG = 4 / GPU;                 // k-blocks per group inside a unit
   constexpr bool TABLE = MODE == LUT;
   constexpr bool Z16 = MODE == ZERO_F16;
-  constexpr bool FINE = MODE == ZFINE;          // fine zero-points (fp16: B = RN(q - z), scale after)
-  constexpr bool HAS_Z = MODE == ZERO_F16 || MODE == ZERO_PACKED || FINE;
-  constexpr int REC = (Z16 ? 4 : 2) * GPU;      // scale record bytes per column
-  constexpr int SW = REC < 4 ? 1 : REC / 4;     // words per scale record
+  constexpr bool FINE = MODE >= ZFINE;          // fp16 zero-points per ZG rows
+  constexpr int ZG = fine_zero_group(MODE);
+  constexpr int ZPL = FINE ? fine_per_lane(ZG) : 0;  // fine zero-points of a lane per unit
+  constexpr int SB = Z16 ? 4 : 2;               // bytes of a lane's scale (+ zero) entry
+  constexpr int REC = SB * GPU;                 // scale record bytes per column
   constexpr int ZREC = 4 * GPU;                 // packed-zero record bytes per column half
-  constexpr bool SCALED = DT == BF16;          // decoded weights already carry the scale
+  constexpr bool SCALED = gemv_scaled<DT, GPU>();
   constexpr bool XS = !SCALED && MODE != LUT && !FINE;  // shared zero-points: remove bias + z via row sums
-  constexpr int ZW = FINE ? 2 : (HAS_Z && !Z16 ? GPU : 1);  // words of a zero record
+  constexpr int ZW = FINE ? (ZPL + 1) / 2 : 1;  // words of a lane's zero entry
   constexpr int NRED = PK == 4 ? 1 : PK == 8 ? 2 : 4;  // reduced values per lane per column tile
 
-  __shared__ uint32_t table[TABLE ? (32 << (2 * BITS)) : 1];
+  __shared__ __attribute__((aligned(16))) uint32_t table[TABLE ? (32 << (2 * BITS)) : 4];
   // LDS of wave w at red + w * WSTRIDE: its activation stage (standard scheme,
   // 4 KiB) while it streams, then its partial results [TN][MR][NRED][64] for
   // the cross-wave reduction.
@@ -148,16 +160,18 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU, MR>() ? 512 : 1024)
   const rsrc_t rc = make_rsrc(a.codes, a.codes_bytes);
   const rsrc_t rx = make_rsrc(a.x, (uint32_t)a.M * a.K * 2);
   const rsrc_t rs = make_rsrc(a.S, a.s_bytes);
-  const rsrc_t rz = make_rsrc(HAS_Z ? a.Z : a.S, HAS_Z ? a.z_bytes : 0u);
+  const rsrc_t rz = make_rsrc(MODE == ZERO_PACKED || FINE ? a.Z : a.S,
+                              MODE == ZERO_PACKED || FINE ? a.z_bytes : 0u);
 
-  // Buffer offsets = per-lane vector part + per-tile scalar part.  The vector
-  // part becomes kOutOfRange for loads that must return zero (rows past M,
-  // tiles past the wave's range).
+  // Activation buffer offsets = per-lane vector part + per-tile scalar part;
+  // the vector part is kOutOfRange for rows past M (those loads return zero).
+  // The MFMA k-block kb of a unit pairs position 8 h' + e of its 32-long k
+  // dimension with unit row 32 h' + 8 kb + e (the tile row map), so:
   //   packed:   lane c -> (m = c / 4, k-block c % 4), one load per 128-row unit;
   //   packed 8: lane c -> (m = c / 2, k-block 2 p + c % 2), load p = 0, 1 of a
   //             unit covering its k-blocks 2 p and 2 p + 1;
   //   standard: lane c -> m = 16 r + c, one load per k-block (the MFMA
-  //             fragment itself: 16 rows, half a cache line each, per load);
+  //             fragment itself: 16 rows, 16 bytes each, per load);
   //   staged:   load j of a unit and row block r reads rows 16 r + 4 j .. + 3,
   //             lane L -> row 16 r + 4 j + L / 16, 16 bytes at k = 8 (L % 16):
   //             four rows x 256 contiguous bytes per load, regrouped into
@@ -169,45 +183,48 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU, MR>() ? 512 : 1024)
 #pragma unroll
     for (int j = 0; j < XJ; ++j) {
       const int xm = PK == 4 ? (c >> 2) : PK == 8 ? (c >> 1) : STAGE ? 16 * r + 4 * j + h : 16 * r + c;
-      const int xk = PK == 4 ? 8 * h + 32 * (c & 3) : PK == 8 ? 8 * h + 32 * (c & 1) : STAGE ? 8 * c : 8 * h;
+      const int xk = PK == 4 ? 32 * h + 8 * (c & 3) : PK == 8 ? 32 * h + 8 * (c & 1) : STAGE ? 8 * c : 32 * h;
       x_lane[r][j] = xm < a.M ? (uint32_t)(xm * a.K + xk) * 2u : kOutOfRange;
     }
   // LDS stage of this wave: row i (0..15) of the unit at 16 chunks of 16 bytes,
   // chunk q stored at position q ^ i (the fragment reads of 16 rows then hit
-  // 16 different bank groups)
+  // 16 different bank groups); the fragment of k-block kb reads chunk 4 h + kb
   u32x4* const stage = (u32x4*)(red + (size_t)wave * WSTRIDE);
   int st_w[XJ], st_r[4];
 #pragma unroll
   for (int j = 0; j < XJ; ++j) st_w[j] = (4 * j + h) * 16 + (c ^ (4 * j + h));
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) st_r[kb] = c * 16 + ((4 * kb + h) ^ c);
+  for (int kb = 0; kb < 4; ++kb) st_r[kb] = c * 16 + ((4 * h + kb) ^ c);
   const uint32_t w_lane = (uint32_t)lane * WPL * 4;
-  const uint32_t s_lane = (uint32_t)c * REC;
-  const uint32_t zp_lane = (uint32_t)(c >> 3) * ZREC;
-  // fine zero records: 8 * hcs bytes per column and unit, this lane's class at 8 hc
-  const int hcs = FINE ? 32 / a.zg : 1;
-  const uint32_t zf_rec = 8u * hcs;
-  const uint32_t zf_lane = (uint32_t)c * zf_rec + 8u * ((h * hcs) >> 2);
+  // metadata: the lane's own group of each unit
+  const int jg = lane_group(h, GPU);
+  const uint32_t s_lane = (uint32_t)(c * REC + jg * SB);
+  const uint32_t zp_lane = (uint32_t)((c >> 3) * ZREC + 4 * jg);
+  const uint32_t zf_lane = FINE ? (uint32_t)((c * fine_per_unit(ZG > 0 ? ZG : 32) + h * ZPL) * 2) : 0u;
   const int nunits = a.ktiles * UPT;
 
   const int kt0 = kslot * a.kt_per_wave;
   const int kt1 = min(kt0 + a.kt_per_wave, a.ktiles);
+  const int kt_safe = min(kt0, a.ktiles - 1);  // an in-range tile for loads whose result is unused
 
   struct Frame {
     uint32_t w[TN][WPL];
     u32x4 xa[MR][NXA];
-    uint32_t s[TN][UPT][SW];                  // scale record (with fp16 zero-points when Z16)
-    uint32_t z[TN][UPT][ZW];                  // packed or fine zero-point record
+    uint32_t s[TN][UPT];                      // the lane's scale (with its fp16 zero-point when Z16)
+    uint32_t z[TN][UPT][ZW];                  // the lane's packed or fine zero-points
   };
 
-  // Loads of tile kt (all of them out of range, hence free, when kt >= kt1).
-  auto load = [&](Frame& f, int kt) {
-    const bool ok = kt < kt1;
-    const int ktc = ok ? kt : kt0;  // keeps the scalar offsets in range
+  // Loads of tile kt.  CHECK: kt may lie past the wave's range; its codes are
+  // then loaded out of range (free), everything else from an in-range tile
+  // (the frame is never computed).  Without CHECK, kt is in range.
+  auto load = [&](Frame& f, int kt, auto check) __attribute__((always_inline)) {
+    constexpr bool CHECK = decltype(check)::value;
+    const bool ok = !CHECK || kt < kt1;
+    const int ktc = ok ? kt : kt_safe;  // keeps the scalar offsets in range
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
       const uint32_t so = (uint32_t)(((nt0 + t) * a.ktiles + ktc) * 64 * WPL * 4);
-      const uint32_t vo = ok ? w_lane : kOutOfRange;
+      const uint32_t vo = CHECK ? (ok ? w_lane : kOutOfRange) : w_lane;
       if constexpr (WPL == 4) {
         const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rc, vo, so, kNontemporal);
         f.w[t][0] = v[0]; f.w[t][1] = v[1]; f.w[t][2] = v[2]; f.w[t][3] = v[3];
@@ -221,13 +238,13 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU, MR>() ? 512 : 1024)
     for (int r = 0; r < MR; ++r) {
 #pragma unroll
       for (int i = 0; i < NXA; ++i) {
-        // packed: load i covers unit i; packed 8: half i % 2 of unit i / 2;
-        // standard: k-block i; staged: load j = i % 4 of unit i / 4
-        const uint32_t xv = ok ? x_lane[r][STAGE ? i % 4 : 0] : kOutOfRange;
+        // packed: load i covers unit i; packed 8: k-blocks 2 (i % 2) + {0, 1}
+        // of unit i / 2; standard: k-block i % 4 of unit i / 4; staged: load
+        // j = i % 4 of unit i / 4
         const uint32_t koff =
-            (uint32_t)(ktc * KT + (PK == 4 ? 128 * i : PK == 8 ? 128 * (i / 2) + 64 * (i % 2)
-                                  : STAGE ? 128 * (i / 4) : 32 * i)) * 2u;
-        f.xa[r][i] = __builtin_amdgcn_raw_buffer_load_b128(rx, xv, koff, 0);
+            (uint32_t)(ktc * KT + (PK == 4 ? 128 * i : PK == 8 ? 128 * (i / 2) + 16 * (i % 2)
+                                  : STAGE ? 128 * (i / 4) : 128 * (i / 4) + 8 * (i % 4))) * 2u;
+        f.xa[r][i] = __builtin_amdgcn_raw_buffer_load_b128(rx, x_lane[r][STAGE ? i % 4 : 0], koff, 0);
       }
     }
 #pragma unroll
@@ -236,20 +253,21 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU, MR>() ? 512 : 1024)
 #pragma unroll
       for (int t = 0; t < TN; ++t) {
         const uint32_t ri = (uint32_t)((nt0 + t) * a.nrec + rec);
-        load_record<REC>(rs, ok ? s_lane : kOutOfRange, ri * 16 * REC, f.s[t][u]);
-        if constexpr (MODE == ZERO_PACKED)
-          load_record<ZREC>(rz, ok ? zp_lane : kOutOfRange, ri * 2 * ZREC, f.z[t][u]);
+        load_record<SB>(rs, s_lane, ri * 16 * REC, &f.s[t][u]);
+        if constexpr (MODE == ZERO_PACKED) load_record<4>(rz, zp_lane, ri * 2 * ZREC, f.z[t][u]);
         if constexpr (FINE)
-          load_record<8>(rz, ok ? zf_lane : kOutOfRange,
-                         (uint32_t)((nt0 + t) * nunits + ktc * UPT + u) * 16u * zf_rec, f.z[t][u]);
+          load_record<2 * ZPL>(rz, zf_lane, (uint32_t)((nt0 + t) * nunits + ktc * UPT + u) * 32u * fine_per_unit(ZG),
+                               f.z[t][u]);
       }
     }
   };
+  const auto checked = std::integral_constant<bool, true>{};
+  const auto unchecked = std::integral_constant<bool, false>{};
 
   Frame fr[PF];
 #pragma unroll
   for (int p = 0; p < PF; ++p) {
-    load(fr[p], kt0 + p);
+    load(fr[p], kt0 + p, checked);
     // packed scheme: frame by frame, in the order the loop reloads them, so
     // that every wait for a frame leaves the later frames in flight
     if constexpr (PACKED) __builtin_amdgcn_sched_barrier(0);
@@ -262,6 +280,9 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU, MR>() ? 512 : 1024)
   const uint32_t* tab = table + (lane & 31);
   const DecodeConsts dk = make_decode_consts<DT>();
 
+  // Scale-after paths: running sums of the scaled unit results.  Exact-decode
+  // paths: MFMA accumulators carried across the whole k-range (acc), summed
+  // into tot at the end.
   float tot[MR][TN][4];
 #pragma unroll
   for (int r = 0; r < MR; ++r)
@@ -269,84 +290,118 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU, MR>() ? 512 : 1024)
     for (int t = 0; t < TN; ++t)
 #pragma unroll
       for (int e = 0; e < 4; ++e) tot[r][t][e] = 0.0f;
+  constexpr int NACC = PACKED ? 4 : 1;  // accumulators per (row block, column tile)
+  f4 acc[SCALED ? MR : 1][TN][SCALED ? NACC : 1];
+  const f4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int r = 0; r < (SCALED ? MR : 1); ++r)
+#pragma unroll
+    for (int t = 0; t < TN; ++t)
+#pragma unroll
+      for (int i = 0; i < (SCALED ? NACC : 1); ++i) acc[r][t][i] = zero4;
 
-  // zero-point of group j of unit u of column tile t
-  auto zero_of = [&](const Frame& f, int t, int u, int j) -> float {
-    if constexpr (MODE == ZERO_F16) return rec_zero16(f.s[t][u], j);
-    else if constexpr (MODE == ZERO_PACKED) return rec_zero_packed(f.z[t][u], j, c);
+  // the lane's zero-point of unit u of column tile t (shared-group modes)
+  auto zero_of = [&](const Frame& f, int t, int u) __attribute__((always_inline)) -> float {
+    if constexpr (MODE == ZERO_F16) return f16_to_f32((uint16_t)(f.s[t][u] >> 16));
+    else if constexpr (MODE == ZERO_PACKED) return (float)((f.z[t][u][0] >> (4 * (c & 7))) & 0xFu);
     else return (float)(1 << (BITS - 1));
   };
+  auto scale_of = [&](const Frame& f, int t, int u) __attribute__((always_inline)) -> float { return f16_to_f32((uint16_t)(f.s[t][u] & 0xFFFFu)); };
+  // fp16 bits of the fine zero-point of k-block kb (0..3 inside the unit)
+  auto fine_bits = [&](const Frame& f, int t, int u, int kb) __attribute__((always_inline)) -> uint32_t {
+    if constexpr (FINE) {
+      const int i = kb * ZPL / 4;
+      return (f.z[t][u][i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+    } else {
+      return 0u;
+    }
+  };
+  // exact-decode parameters of unit u of column tile t
+  auto params = [&](const Frame& f, int t, int u) __attribute__((always_inline)) {
+    ExactParams p;
+    p.s = scale_of(f, t, u);
+    p.s_h = h2s(p.s);
+    p.sz = (MODE == LUT || FINE) ? 0.0f : p.s * zero_of(f, t, u);
+    p.nz_h = h2s(0.0f);
+    return p;
+  };
 
-  auto compute = [&](const Frame& f) {
-    const f4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+  auto compute = [&](const Frame& f) __attribute__((always_inline)) {
     sfor<UPT>([&](auto uc) {
       constexpr int u = decltype(uc)::value;
+      ExactParams prm[TN];
+      if constexpr (SCALED) {
+#pragma unroll
+        for (int t = 0; t < TN; ++t) prm[t] = params(f, t, u);
+      }
       if constexpr (PK == 8) {
         // Two A operands per unit (p = 0, 1: rows 2m + j hold k-block 2p + j);
         // accumulator kb keeps the rows 2m + kb % 2, i.e. the elements e with
         // e % 2 == kb % 2 (row 4h + e = 2m + j: m = 2h + e / 2, j = e % 2).
-        f4 acc[TN][4];
+        f4 ua[TN][4];
         sfor<4>([&](auto kbc) {
           constexpr int kb = decltype(kbc)::value;
 #pragma unroll
           for (int t = 0; t < TN; ++t) {
-            const u32x4 b = decode_frag<BITS, DT, MODE, 4 * u + kb>(
-                f.w[t], tab, dk, FINE ? fine_zero_bits(f.z[t][u], kb) : 0u,
-                SCALED ? rec_scale<Z16>(f.s[t][u], kb / KBPG) : 0.0f,
-                SCALED && !TABLE && !FINE ? zero_of(f, t, u, kb / KBPG) : 0.0f);
-            acc[t][kb] = mfma16<DT>(f.xa[0][2 * u + kb / 2], b, zero4);
+            const u32x4 b = decode_frag<BITS, DT, MODE, 4 * u + kb, SCALED>(f.w[t], tab, dk, fine_bits(f, t, u, kb),
+                                                                             prm[t]);
+            if constexpr (SCALED) acc[0][t][kb] = mfma16<DT>(f.xa[0][2 * u + kb / 2], b, acc[0][t][kb]);
+            else ua[t][kb] = mfma16<DT>(f.xa[0][2 * u + kb / 2], b, zero4);
           }
         });
-        f4 xs[2] = {zero4, zero4};
-        if constexpr (XS) {
+        if constexpr (!SCALED) {
+          f4 xs[2] = {zero4, zero4};
+          if constexpr (XS) {
 #pragma unroll
-          for (int p = 0; p < 2; ++p) xs[p] = mfma16<DT>(f.xa[0][2 * u + p], ones_frag<DT>(), zero4);
-        }
+            for (int p = 0; p < 2; ++p) xs[p] = mfma16<DT>(f.xa[0][2 * u + p], ones_frag<DT>(), zero4);
+          }
 #pragma unroll
-        for (int t = 0; t < TN; ++t) {
+          for (int t = 0; t < TN; ++t) {
+            const float s = scale_of(f, t, u);
+            const float cz = XS ? zero_corr<DT>(zero_of(f, t, u)) : 0.0f;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
+            for (int e = 0; e < 4; ++e) {
 #pragma unroll
-            for (int kb = e & 1; kb < 4; kb += 2) {
-              const int j = kb / KBPG;
-              const float s = SCALED ? 1.0f : rec_scale<Z16>(f.s[t][u], j);
-              float v = acc[t][kb][e];
-              if constexpr (XS) v = __builtin_fmaf(-zero_corr<DT>(zero_of(f, t, u, j)), xs[kb / 2][e], v);
-              tot[0][t][e] = __builtin_fmaf(s, v, tot[0][t][e]);
+              for (int kb = e & 1; kb < 4; kb += 2) {
+                float v = ua[t][kb][e];
+                if constexpr (XS) v = __builtin_fmaf(-cz, xs[kb / 2][e], v);
+                tot[0][t][e] = __builtin_fmaf(s, v, tot[0][t][e]);
+              }
             }
           }
         }
       } else if constexpr (PACKED) {
         // One A operand for the 4 k-blocks of the unit; accumulator kb keeps row 4m + kb.
-        f4 acc[TN][4];
+        f4 ua[TN][4];
         sfor<4>([&](auto kbc) {
           constexpr int kb = decltype(kbc)::value;
 #pragma unroll
           for (int t = 0; t < TN; ++t) {
-            const u32x4 b = decode_frag<BITS, DT, MODE, 4 * u + kb>(
-                f.w[t], tab, dk, FINE ? fine_zero_bits(f.z[t][u], kb) : 0u,
-                SCALED ? rec_scale<Z16>(f.s[t][u], kb / KBPG) : 0.0f,
-                SCALED && !TABLE && !FINE ? zero_of(f, t, u, kb / KBPG) : 0.0f);
-            acc[t][kb] = mfma16<DT>(f.xa[0][u], b, zero4);
+            const u32x4 b = decode_frag<BITS, DT, MODE, 4 * u + kb, SCALED>(f.w[t], tab, dk, fine_bits(f, t, u, kb),
+                                                                             prm[t]);
+            if constexpr (SCALED) acc[0][t][kb] = mfma16<DT>(f.xa[0][u], b, acc[0][t][kb]);
+            else ua[t][kb] = mfma16<DT>(f.xa[0][u], b, zero4);
           }
         });
-        f4 xs = zero4;
-        if constexpr (XS) xs = mfma16<DT>(f.xa[0][u], ones_frag<DT>(), zero4);
-        // element e of this lane = row 4m + e = k-block e of the unit
+        if constexpr (!SCALED) {
+          f4 xs = zero4;
+          if constexpr (XS) xs = mfma16<DT>(f.xa[0][u], ones_frag<DT>(), zero4);
+          // element e of this lane = row 4m + e = k-block e of the unit
 #pragma unroll
-        for (int t = 0; t < TN; ++t) {
+          for (int t = 0; t < TN; ++t) {
+            const float s = scale_of(f, t, u);
+            const float cz = XS ? zero_corr<DT>(zero_of(f, t, u)) : 0.0f;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int j = e / KBPG;
-            const float s = SCALED ? 1.0f : rec_scale<Z16>(f.s[t][u], j);
-            float v = acc[t][e][e];
-            if constexpr (XS) v = __builtin_fmaf(-zero_corr<DT>(zero_of(f, t, u, j)), xs[e], v);
-            tot[0][t][e] = __builtin_fmaf(s, v, tot[0][t][e]);
+            for (int e = 0; e < 4; ++e) {
+              float v = ua[t][e][e];
+              if constexpr (XS) v = __builtin_fmaf(-cz, xs[e], v);
+              tot[0][t][e] = __builtin_fmaf(s, v, tot[0][t][e]);
+            }
           }
         }
       } else {
         // the unit's activations as MFMA fragments (k-block kb: rows 16 r + c,
-        // k = 32 kb + 8 h ..), regrouped through the LDS stage when staged
+        // unit rows 32 h + 8 kb ..), regrouped through the LDS stage when staged
         u32x4 xf[MR][4];
 #pragma unroll
         for (int r = 0; r < MR; ++r) {
@@ -360,54 +415,57 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU, MR>() ? 512 : 1024)
             for (int kb = 0; kb < 4; ++kb) xf[r][kb] = f.xa[r][4 * u + kb];
           }
         }
-        sfor<GPU>([&](auto gc) {
-          constexpr int gi = decltype(gc)::value;
-          f4 acc[MR][TN];
-          f4 xs[MR];
+        f4 ua[MR][TN];
+        f4 xs[MR];
 #pragma unroll
-          for (int r = 0; r < MR; ++r) {
-            xs[r] = zero4;
+        for (int r = 0; r < MR; ++r) {
+          xs[r] = zero4;
 #pragma unroll
-            for (int t = 0; t < TN; ++t) acc[r][t] = zero4;
-          }
-          sfor<KBPG>([&](auto kc) {
-            constexpr int kb = 4 * u + gi * KBPG + decltype(kc)::value;  // k-block inside the tile
-#pragma unroll
-            for (int t = 0; t < TN; ++t) {
-              const u32x4 b = decode_frag<BITS, DT, MODE, kb>(
-                  f.w[t], tab, dk, FINE ? fine_zero_bits(f.z[t][u], kb - 4 * u) : 0u,
-                  SCALED ? rec_scale<Z16>(f.s[t][u], gi) : 0.0f,
-                  SCALED && !TABLE && !FINE ? zero_of(f, t, u, gi) : 0.0f);
-#pragma unroll
-              for (int r = 0; r < MR; ++r) acc[r][t] = mfma16<DT>(xf[r][kb - 4 * u], b, acc[r][t]);
-            }
-            if constexpr (XS)
-#pragma unroll
-              for (int r = 0; r < MR; ++r) xs[r] = mfma16<DT>(xf[r][kb - 4 * u], ones_frag<DT>(), xs[r]);
-          });
+          for (int t = 0; t < TN; ++t) ua[r][t] = zero4;
+        }
+        sfor<4>([&](auto kc) {
+          constexpr int kb = decltype(kc)::value;
 #pragma unroll
           for (int t = 0; t < TN; ++t) {
-            const float s = SCALED ? 1.0f : rec_scale<Z16>(f.s[t][u], gi);
-            const float cz = XS ? zero_corr<DT>(zero_of(f, t, u, gi)) : 0.0f;
+            const u32x4 b = decode_frag<BITS, DT, MODE, 4 * u + kb, SCALED>(f.w[t], tab, dk, fine_bits(f, t, u, kb),
+                                                                             prm[t]);
+#pragma unroll
+            for (int r = 0; r < MR; ++r) {
+              if constexpr (SCALED) acc[r][t][0] = mfma16<DT>(xf[r][kb], b, acc[r][t][0]);
+              else ua[r][t] = mfma16<DT>(xf[r][kb], b, ua[r][t]);
+            }
+          }
+          if constexpr (XS)
+#pragma unroll
+            for (int r = 0; r < MR; ++r) xs[r] = mfma16<DT>(xf[r][kb], ones_frag<DT>(), xs[r]);
+        });
+        if constexpr (!SCALED) {
+#pragma unroll
+          for (int t = 0; t < TN; ++t) {
+            const float s = scale_of(f, t, u);
+            const float cz = XS ? zero_corr<DT>(zero_of(f, t, u)) : 0.0f;
 #pragma unroll
             for (int r = 0; r < MR; ++r)
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
-                float v = acc[r][t][e];
+                float v = ua[r][t][e];
                 if constexpr (XS) v = __builtin_fmaf(-cz, xs[r][e], v);
                 tot[r][t][e] = __builtin_fmaf(s, v, tot[r][t][e]);
               }
           }
-        });
+        }
       }
     });
   };
 
-  // Stream this wave's k-range PF tiles ahead.  Inside the loop every frame is
-  // a valid tile and every load unconditional (the last group's loads past the
-  // range are out of range and free); the last group is computed after it.
-  const int niter = kt1 > kt0 ? (kt1 - kt0 + PF - 1) / PF : 0;
-  for (int it = 0; it + 1 < niter; ++it) {
+  // Stream this wave's k-range PF tiles ahead.  Inside the loops every frame
+  // is a valid tile and every load unconditional; the first loop's reloads all
+  // lie in range (no checks), the second (at most one iteration) reloads past
+  // the range with checked loads, and the last group is computed after them.
+  const int T = kt1 > kt0 ? kt1 - kt0 : 0;
+  const int niter = (T + PF - 1) / PF;
+  const int nfast = T >= PF ? T / PF - 1 : 0;
+  auto step = [&](int it, auto check) __attribute__((always_inline)) {
     const int kt = kt0 + it * PF;
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
@@ -418,15 +476,30 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU, MR>() ? 512 : 1024)
       // neutral at M = 1 and for the standard scheme, which keeps the
       // scheduler's order
       if constexpr (PACKED) __builtin_amdgcn_sched_barrier(0);
-      load(fr[p], kt + p + PF);
+      load(fr[p], kt + p + PF, check);
       if constexpr (PACKED) __builtin_amdgcn_sched_barrier(0);
     }
-  }
+  };
+  for (int it = 0; it < nfast; ++it) step(it, unchecked);
+  for (int it = nfast; it + 1 < niter; ++it) step(it, checked);
   if (niter > 0) {
     const int kt = kt0 + (niter - 1) * PF;
 #pragma unroll
     for (int p = 0; p < PF; ++p)
       if (kt + p < kt1) compute(fr[p]);
+  }
+  if constexpr (SCALED) {
+    // packed: element e is the diagonal row 4m + e (k-block e); packed 8:
+    // rows 2m + e % 2 of the two accumulators of that parity
+#pragma unroll
+    for (int r = 0; r < MR; ++r)
+#pragma unroll
+      for (int t = 0; t < TN; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          tot[r][t][e] = PK == 4 ? acc[r][t][PACKED ? e : 0][e]
+                       : PK == 8 ? acc[r][t][PACKED ? (e & 1) : 0][e] + acc[r][t][PACKED ? (e & 1) + 2 : 0][e]
+                                 : acc[r][t][0][e];
   }
 
   // Cross-wave reduction and store.
@@ -483,11 +556,17 @@ wq_status run(GemvArgs g, int grid, hipStream_t s) {
 }
 
 // Launch shape (measured on MI355X for the decode layer shapes): a few
-// thousand waves over the grid (about 4096 for the packed schemes, 3072 for
-// one block of 16 rows, 1536 for two), each streaming an equal share of K;
-// the prefetch depth grows with the tiles a wave streams (deeper prefetch
-// costs registers and out-of-range tail loads, so short ranges keep it at 2).
-inline int pick_waves(int grid, int ktiles, bool table, int wmax, long plain = 3072L) {
+// thousand waves over the grid (about 6144 for the packed schemes, 3072 for
+// one block of 16 rows, 1536 for two, 12288 for table codes), each streaming
+// an equal share of K; the prefetch depth is 2 except for workgroups of one
+// or two waves with long k-ranges (see run_pf).
+inline int pick_waves_auto(int grid, int ktiles, bool table, int wmax, long plain);
+// The waves of a launch: the override when given (clamped to wmax), else the heuristic.
+inline int pick_waves(const GemvArgs& g, int grid, bool table, int wmax, long plain = 3072L) {
+  if (g.force_waves > 0) return g.force_waves < wmax ? g.force_waves : wmax;
+  return pick_waves_auto(grid, g.ktiles, table, wmax, plain);
+}
+inline int pick_waves_auto(int grid, int ktiles, bool table, int wmax, long plain) {
   // about `plain` waves in flight (12288 when each workgroup fills an LDS code
   // table, which caps the workgroups per CU), at most 32 k-tiles per wave,
   // at least 2
@@ -500,8 +579,14 @@ template <int DT, int BITS, int MODE, int TN, int GPU, int PK, bool SWIGLU, int 
 wq_status run_pf(GemvArgs g, int grid, hipStream_t s) {
   const int tpw = g.kt_per_wave;
   if constexpr (PK != 0) {
-    if (tpw >= 8) return run<DT, BITS, MODE, TN, GPU, PK, 4, SWIGLU, MR, false>(g, grid, s);
-    if (tpw >= 5) return run<DT, BITS, MODE, TN, GPU, PK, 3, SWIGLU, MR, false>(g, grid, s);
+    // Prefetch depth (tiles in flight per wave): deep only when a workgroup
+    // has one or two waves, each streaming a long k-range; with four or more
+    // waves two tiles ahead measured best or level on every decode shape
+    // (16 waves at four ahead lost up to 30 %: the frames cost half the
+    // occupancy), one wave per SIMD at four ahead gained up to 20 %.
+    const int pf = g.force_pf ? g.force_pf : g.waves > 2 ? 2 : tpw >= 8 ? 4 : tpw >= 5 ? 3 : 2;
+    if (pf >= 4) return run<DT, BITS, MODE, TN, GPU, PK, 4, SWIGLU, MR, false>(g, grid, s);
+    if (pf == 3) return run<DT, BITS, MODE, TN, GPU, PK, 3, SWIGLU, MR, false>(g, grid, s);
   }
   return run<DT, BITS, MODE, TN, GPU, PK, 2, SWIGLU, MR, STAGE>(g, grid, s);
 }
@@ -528,7 +613,7 @@ wq_status pick_standard(GemvArgs g, hipStream_t s) {
     // size; measured faster than matching its per-wave work with workgroups
     // twice as large.
     const int wmax = gemv_big_frames<BITS, 1, GPU, MR>() ? 8 : 16;
-    const int kw = max(1, pick_waves(ntiles, g.ktiles, MODE == LUT, wmax) / 2);  // waves per column tile
+    const int kw = max(1, pick_waves(g, ntiles, MODE == LUT, wmax) / 2);  // waves per column tile
     g.waves = 2 * kw;
     g.kt_per_wave = (g.ktiles + kw - 1) / kw;
     return run_standard<DT, BITS, MODE, 1, GPU, true, MR>(g, ntiles / 2, s);
@@ -560,7 +645,7 @@ wq_status pick_standard(GemvArgs g, hipStream_t s) {
     // two row blocks: about half the waves, each streaming twice the k-range
     // (M = 32: 10-13 % faster on the 12288- and 22016-column layers, equal on
     // the others; at 16 rows the same target loses up to 10 %)
-    g.waves = pick_waves(grid, g.ktiles, MODE == LUT, big ? 8 : 16, MR == 2 ? 1536L : 3072L);
+    g.waves = pick_waves(g, grid, MODE == LUT, big ? 8 : 16, MR == 2 ? 1536L : 3072L);
     g.kt_per_wave = (g.ktiles + g.waves - 1) / g.waves;
     if constexpr (TNMAX >= 4)
       if (tn == 4) return run_standard<DT, BITS, MODE, 4, GPU, false, MR>(g, grid, s);
@@ -595,15 +680,16 @@ wq_status pick_shape(GemvArgs g, hipStream_t s) {
   const int wmax = gemv_big_frames<BITS, 1, GPU, 1>() ? 8 : 16;
   const bool pk8 = g.M > 4;
   if constexpr (SWIGLU) {
-    const int kw = max(1, pick_waves(ntiles, g.ktiles, MODE == LUT, wmax) / 2);  // waves per column tile
+    const int kw = max(1, pick_waves(g, ntiles, MODE == LUT, wmax) / 2);  // waves per column tile
     g.waves = 2 * kw;
     g.kt_per_wave = (g.ktiles + kw - 1) / kw;
     return pk8 ? run_pf<DT, BITS, MODE, 1, GPU, 8, true, 1>(g, ntiles / 2, s)
                : run_pf<DT, BITS, MODE, 1, GPU, 4, true, 1>(g, ntiles / 2, s);
   } else {
-    // about 4096 waves (3072 measured 3-10 % slower on the 12288-, 24576- and
-    // 28672-column layers, equal elsewhere)
-    g.waves = pick_waves(ntiles, g.ktiles, MODE == LUT, wmax, 4096L);
+    // about 6144 waves (4096 measured 3-4 % slower on the 12288- and
+    // 22016-column layers at M = 1, 3072 3-10 % slower on the 12288-, 24576-
+    // and 28672-column layers, equal elsewhere)
+    g.waves = pick_waves(g, ntiles, MODE == LUT, wmax, 6144L);
     g.kt_per_wave = (g.ktiles + g.waves - 1) / g.waves;
     return pk8 ? run_pf<DT, BITS, MODE, 1, GPU, 8, false, 1>(g, ntiles, s)
                : run_pf<DT, BITS, MODE, 1, GPU, 4, false, 1>(g, ntiles, s);
@@ -629,13 +715,13 @@ wq_status WQ_CAT(launch_gemv_, WQ_VARIANT)(const ProductArgs& p) {
   g.M = p.M; g.N = p.N; g.K = p.K; g.nrec = L.nrec; g.upr = (L.gsz > 128 ? L.gsz : 128) / 128;
   g.ktiles = L.ktiles;
   g.waves = 1; g.kt_per_wave = 0;
+  g.force_waves = p.waves; g.force_pf = p.pf;
   g.ldy = p.swiglu ? p.N / 2 : p.N;
-  g.zg = fine_zero_group(p.mode);
   const int gpu = L.gsz >= 128 ? 1 : 128 / L.gsz;  // groups per 128-row unit
   wq_status st = WQ_EINVAL;
-  sfor<5>([&](auto mi) {
+  sfor<7>([&](auto mi) {  // the ABI mode itself: fine zero-points keep their group
     constexpr int MODE = decltype(mi)::value;
-    if (MODE != kernel_mode(p.mode)) return;
+    if (MODE != p.mode) return;
     if (p.swiglu) {
       if (gpu == 1) st = pick_shape<D, B, MODE, 1, true>(g, p.stream);
       else if (gpu == 2) st = pick_shape<D, B, MODE, 2, true>(g, p.stream);

@@ -10,10 +10,16 @@
 // reads contiguous memory.  Inside a tile, lane l (0..63) of a wave owns
 // WPL consecutive 32-bit words (WPL = 4, or 3 for 3-bit codes): one 128-bit
 // (96-bit) coalesced load per lane, 1 KiB (768 B) per wave.  Lane l = 16h + c
-// holds column c of the tile and, for every 32-row k-block kb of the tile,
-// rows 32kb + 8h + e (e = 0..7): exactly the B operand a 16x16x32 MFMA wants
-// from that lane.  Rows are in act-order-sorted order when a permutation is
-// used.
+// holds column c of the tile.  Its codes form k-blocks kb of 8 elements e, one
+// k-block per MFMA: element e of k-block kb is row
+//     128 (kb / 4) + 32 h + 8 (kb % 4) + e
+// of the tile, so the 8 rows a lane feeds one 16x16x32 MFMA are consecutive
+// and the four lanes of a column (h = 0..3) hold the four 32-row quarters of
+// every 128-row unit.  A lane therefore meets exactly one scale group per unit
+// for every group size from 32 rows up (quarter h lies in group h * GPU / 4 of
+// the unit, GPU = groups per unit).  The MFMA pairs A and B by position inside
+// its 32-long k dimension, so the activation fragments are loaded with the
+// same row map.  Rows are in act-order-sorted order when a permutation is used.
 //
 // Element e of k-block kb inside the lane's words:
 //   4-bit uniform  word kb, nibble (e%2)*4 + e/2   (pairs (e, e+1) sit in the
@@ -25,10 +31,9 @@
 //                  (lo = even element); pairs 0..14 at bits 6*(p%5) of word
 //                  p/5, pair 15 split over bits 30..31 of words 0, 1, 2.
 //
-// Scales / zero-points.  Re-laid so that one vector load per 128-row unit of K
-// brings a lane everything it needs for its column.  With GPU = groups per
-// unit (1 for groups of 128 rows or more, else 128 / group_size) and a record
-// per (column tile, unit or group, column):
+// Scales / zero-points.  With GPU = groups per 128-row unit (1 for groups of
+// 128 rows or more, else 128 / group_size) and a record per (column tile,
+// unit or group, column):
 //   scale records   fp16 [N/16][R][16][GPU]          R = K / max(group, 128)
 //                   or, with fp16 zero-points, (scale, zero) fp16 pairs
 //                   [N/16][R][16][GPU][2] (one record holds both);
@@ -36,20 +41,19 @@
 //                   zero-points of columns 8h..8h+7 of group j as nibbles
 //                   (whatever the code width).
 // Record r covers unit r when groups are smaller than 128 rows, else group r.
+// Lane (c, h) reads only entry j = h * GPU / 4 of its column's record.
 //
 // Fine zero-points (zero groups of ZG = 8, 16 or 32 rows, apart from the
-// scale groups): fp16 [N/16][K/128][16][HC][4] with HC = 32 / ZG row classes.
-// Lane (c, h) of a wave needs, for k-block kb of a 128-row unit, the zero of
-// rows 32 kb + 8 h .. + 7 (one zero group); lanes h with the same class
-// hc = h * HC / 4 share it.  Entry [nt][u][c][hc][kb] is that zero, so a lane
-// reads its four (one per k-block) with one 8-byte load at
-// ((nt * K/128 + u) * 16 + c) * 8 HC + 8 hc.  Scales then use the symmetric
-// mode's records.
+// scale groups): fp16 [N/16][K/128][16][128/ZG], entry [nt][u][c][i] the zero
+// of rows 128 u + ZG i .. + ZG - 1 of column 16 nt + c.  Lane (c, h) covers
+// rows 32 h .. 32 h + 31 of the unit: entries ZPL h .. ZPL h + ZPL - 1 with
+// ZPL = 32 / ZG (one 8-, 4- or 2-byte load), k-block kb using entry
+// ZPL h + kb * ZPL / 4.
 #pragma once
 #include <stddef.h>
 #include <stdint.h>
 
-#define WQ_HD __host__ __device__ inline
+#define WQ_HD __host__ __device__ constexpr
 
 namespace wq {
 
@@ -66,6 +70,13 @@ WQ_HD int tile_bytes(int bits) { return 256 * words_per_lane(bits); }
 WQ_HD int kblocks_per_tile(int bits) { return tile_k(bits) / 32; }
 
 WQ_HD int groups_per_unit(int gsz) { return gsz >= 128 ? 1 : 128 / gsz; }
+// Row of element e of k-block kb (within its tile) for lane half h.
+WQ_HD int tile_row(int kb, int h, int e) { return 128 * (kb / 4) + 32 * h + 8 * (kb % 4) + e; }
+// Group inside its unit that lane half h meets (gpu = groups per unit).
+WQ_HD int lane_group(int h, int gpu) { return (h * gpu) >> 2; }
+// Fine zero-points: entries per column and unit, and per lane.
+WQ_HD int fine_per_unit(int zg) { return 128 / zg; }
+WQ_HD int fine_per_lane(int zg) { return 32 / zg; }
 // Metadata record of the 128-row unit `unit` (see above).
 WQ_HD int meta_record(int unit, int gsz) { return (unit * 128) / (gsz > 128 ? gsz : 128); }
 
@@ -103,7 +114,7 @@ inline Layout make_layout(int K, int N, int bits, int group_size, int mode) {
   L.scales_bytes = (size_t)L.ntiles * L.nrec * 16 * L.rec_bytes;
   L.zeros_off = align256(L.scales_off + L.scales_bytes);
   L.zeros_bytes = mode == ZERO_PACKED ? (size_t)L.ntiles * L.nrec * 2 * L.gpu * 4 : 0;
-  if (fine_zero_group(mode)) L.zeros_bytes = (size_t)L.ntiles * (K / 128) * 16 * (256 / fine_zero_group(mode));
+  if (fine_zero_group(mode)) L.zeros_bytes = (size_t)L.ntiles * (K / 128) * 16 * 2 * fine_per_unit(fine_zero_group(mode));
   L.total = align256(L.zeros_off + L.zeros_bytes);
   return L;
 }
