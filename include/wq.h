@@ -21,7 +21,14 @@
  *     (Triton GPTQ page, "How It Works").
  * The dequantised weight is defined as one round-to-nearest-even of the exact
  * s*(q-z) or s*T[q] to the activation dtype (a reading: the pages give no
- * formula); wq_dequant_debug produces exactly those bits.
+ * formula); wq_dequant_debug produces exactly those bits.  The products
+ * multiply those weights (with fp16 activations and one scale group per 128
+ * rows the decode-sized product applies s after the MFMA, which for one-hot
+ * rows of x gives the same bits), except where fp16 activations meet fp16
+ * zero-points in two places -- the large-M product (shared or fine zero-points)
+ * and the decode-sized product with fine zero-points and one scale group per
+ * 128 rows -- which multiply RN(s*RN(q-z)): different bits only where q - z
+ * needs more than 11 significant bits.
  *
  * Conventions shared by every entry point:
  *   - Pointers named *_host are host memory; every other pointer is device

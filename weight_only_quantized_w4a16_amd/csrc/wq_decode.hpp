@@ -340,6 +340,27 @@ __device__ inline void fill_pair_table(uint32_t* table, const uint16_t* lut, int
   }
 }
 
+// The same table from values already in registers: lane i (< 2^BITS) of
+// every wave holds T[i] in the low 16 bits of tval (one load per lane, issued
+// before anything else, so its latency overlaps the first weight loads); the
+// pairs are gathered with cross-lane shuffles.  Every lane of the workgroup
+// calls this; `table` must be 16-byte aligned.
+template <int BITS, int COPIES = 32>
+__device__ inline void fill_pair_table_lanes(uint32_t* table, uint32_t tval, int tid, int nthreads) {
+  static_assert(COPIES % 4 == 0, "copies come in 16-byte chunks");
+  constexpr int n = 1 << (2 * BITS);
+  constexpr int mask = (1 << BITS) - 1;
+  constexpr int CPE = COPIES / 4;  // chunks per entry
+  for (int base = 0; base < n * CPE; base += nthreads) {
+    const int i = base + tid;
+    const int idx = (i / CPE) & (n - 1);
+    // shuffles with every lane active (the source lanes 0 .. 2^BITS - 1 always are)
+    const uint32_t lo = (uint32_t)__shfl((int)tval, idx & mask), hi = (uint32_t)__shfl((int)tval, idx >> BITS);
+    const uint32_t v = (lo & 0xFFFFu) | (hi << 16);
+    if (i < n * CPE) *(u32x4*)(table + 4 * i) = u32x4{v, v, v, v};
+  }
+}
+
 // Zero-point / table parameters of one (group, column) for the exact path.
 struct ExactParams {
   float s;        // scale

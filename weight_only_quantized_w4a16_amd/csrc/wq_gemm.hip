@@ -15,11 +15,16 @@
 //    reads of 16 rows hit 16 different bank groups;
 //  * each wave loads the packed codes of its columns straight from global
 //    memory -- the tile layout already is the MFMA B operand, one 128-bit load
-//    per lane per tile -- and dequantises them in registers with the exact
-//    decode (RN(s*(q - z)) or RN(s*T[q]) in the activation dtype), so the
-//    product multiplies exactly the weights the debug dump writes;
+//    per lane per tile -- and dequantises them in registers.  The product
+//    multiplies exactly the weights the debug dump writes (RN(s*(q - z)) or
+//    RN(s*T[q]) in the activation dtype) for every decode but one: with fp16
+//    activations and fp16 zero-points (shared or fine) q - z is formed in
+//    fp16 first, RN(s*RN(q - z)), which differs only where q - z needs more
+//    than 11 significant bits (never for zero-points in [8, 16); for those in
+//    [4, 8) where |q - z| >= 8);
 //  * with one scale per column and fp16 symmetric codes, the scale moves to
-//    the epilogue (the weight operand is then the exact integer q - 8);
+//    the epilogue (the weight operand is then the exact integer q - 8, and
+//    (q - 8) * s is exact in fp32 before the output rounding);
 //  * the weights are the MFMA A operand and the activations B, so each lane
 //    ends with four consecutive outputs of one row: 8-byte stores.
 #include <hip/hip_runtime.h>

@@ -157,6 +157,12 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU, MR>() ? 512 : 1024)
   const int nt0 = SWIGLU ? 2 * blockIdx.x + (wave & 1) : blockIdx.x * TN;  // first column tile of this wave
   const int kslot = SWIGLU ? wave >> 1 : wave;                             // k-range of this wave
 
+  // table codes: lane i of every wave loads T[i] first of all (lanes past the
+  // table read zero)
+  uint32_t lut_lane = 0;
+  if constexpr (TABLE)
+    lut_lane = __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(a.lut, 2u << BITS), (uint32_t)lane * 2u, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);  // keep it ahead of the weight loads
   const rsrc_t rc = make_rsrc(a.codes, a.codes_bytes);
   const rsrc_t rx = make_rsrc(a.x, (uint32_t)a.M * a.K * 2);
   const rsrc_t rs = make_rsrc(a.S, a.s_bytes);
@@ -274,7 +280,7 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU, MR>() ? 512 : 1024)
   }
 
   if constexpr (TABLE) {
-    fill_pair_table<BITS, false>(table, a.lut, threadIdx.x, a.waves * 64);  // fp16 values
+    fill_pair_table_lanes<BITS>(table, lut_lane, threadIdx.x, a.waves * 64);  // fp16 values
     __syncthreads();
   }
   const uint32_t* tab = table + (lane & 31);
@@ -689,6 +695,9 @@ wq_status pick_shape(GemvArgs g, hipStream_t s) {
     // about 6144 waves (4096 measured 3-4 % slower on the 12288- and
     // 22016-column layers at M = 1, 3072 3-10 % slower on the 12288-, 24576-
     // and 28672-column layers, equal elsewhere)
+    // (two column tiles per wave, sharing the activation loads and, for table
+    // codes, the LDS table fill of half as many workgroups, measured 3-35 %
+    // slower on every M = 1 layer of the workloads)
     g.waves = pick_waves(g, ntiles, MODE == LUT, wmax, 6144L);
     g.kt_per_wave = (g.ktiles + g.waves - 1) / g.waves;
     return pk8 ? run_pf<DT, BITS, MODE, 1, GPU, 8, false, 1>(g, ntiles, s)
