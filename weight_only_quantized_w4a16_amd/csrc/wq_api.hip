@@ -33,10 +33,21 @@ __device__ inline void place_code(uint32_t* w, int kb, int e, uint32_t q) {
   if (BITS == 4) {
     const int nib = TABLE_LAYOUT ? e : (e % 2) * 4 + e / 2;
     w[kb] |= q << (4 * nib);
+  } else if (BITS == 2 && TABLE_LAYOUT) {
+    // four codes byte-aligned: byte e % 4, bits 2 (2 (kb % 2) + e / 4)
+    w[kb / 2] |= q << (8 * (e % 4) + 2 * (2 * (kb % 2) + e / 4));
   } else if (BITS == 2) {
     const int i = 4 * (kb % 2) + e / 2;
-    const int pos = TABLE_LAYOUT ? 4 * i + 2 * (e % 2) : 16 * (e % 2) + 2 * i;
-    w[kb / 2] |= q << pos;
+    w[kb / 2] |= q << (16 * (e % 2) + 2 * i);
+  } else if (TABLE_LAYOUT) {
+    // 3-bit table codes, four codes byte-aligned: group x = 2 kb + e / 4, byte e % 4
+    const int x = 2 * kb + e / 4, b = e % 4;
+    if (x < 6) {
+      w[x / 2] |= q << (8 * b + 3 * (x % 2));
+    } else {
+      w[x - 6] |= (q & 3u) << (8 * b + 6);
+      w[2] |= ((q >> 2) & 1u) << (8 * b + (x - 6) + 6);
+    }
   } else {
     const int p = 4 * kb + e / 2;
     const int fb = 3 * (e % 2);  // bit offset of this code inside the 6-bit pair field
@@ -141,12 +152,19 @@ __global__ __launch_bounds__(64) void dequant_debug_kernel(const uint8_t* __rest
   constexpr int KT = BITS == 2 ? 256 : 128;
   constexpr int KB = KT / 32;
   constexpr int WPL = BITS == 3 ? 3 : 4;
-  __shared__ uint32_t table[MODE == LUT ? (32 << (2 * BITS)) : 1];
+  constexpr bool LDS_TABLE = MODE == LUT && BITS == 4;
+  __shared__ __attribute__((aligned(16))) uint32_t table[LDS_TABLE ? (32 << (2 * BITS)) : 4];
   const int lane = threadIdx.x, kt = blockIdx.x, nt = blockIdx.y;
   const int c = lane & 15, h = lane >> 4;
-  if constexpr (MODE == LUT) {
+  if constexpr (LDS_TABLE) {
     fill_pair_table<BITS, false>(table, lut, lane, 64);
     __syncthreads();
+  }
+  // 2- and 3-bit tables: the values as pairs in registers (lane i loads T[i])
+  uint32_t Tp[4] = {0u, 0u, 0u, 0u};
+  if constexpr (MODE == LUT && BITS < 4) {
+    const uint32_t tv = lane < (1 << BITS) ? lut[lane] : 0u;
+    table_pairs_from_lanes<BITS>(tv, Tp);
   }
   const uint32_t* tab = table + (lane & 31);
   const DecodeConsts dk = make_decode_consts<DT>();
@@ -183,6 +201,7 @@ __global__ __launch_bounds__(64) void dequant_debug_kernel(const uint8_t* __rest
     p.s = sv;
     p.s_h = h2s(p.s);
     p.sz = MODE == LUT ? 0.0f : p.s * zv;
+    if constexpr (MODE == LUT && BITS < 4) p.rt = scaled_reg_table<BITS, DT>(Tp, p.s, dk);
     const u32x4 v = exact_frag<BITS, DT, MODE, kb>(words, p, tab, dk);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {

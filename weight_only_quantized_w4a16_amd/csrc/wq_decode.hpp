@@ -141,6 +141,74 @@ __device__ inline uint32_t pair6(const uint32_t* w) {
 }
 
 // ---------------------------------------------------------------------------
+// Register tables of 2- and 3-bit table codes.  The 4 or 8 values of a table
+// (the layer's T[q], or the dequantised RN(s * T[q]) of one group and column)
+// are held as two byte planes: L[i] holds the low bytes and H[i] the high
+// bytes of entries 4i .. 4i + 3.  One v_perm_b32 then looks up the low (or
+// high) bytes of four codes at once (its selector bytes 0..7 pick bytes of
+// {L[1], L[0]}), and two more interleave them into the two value pairs an MFMA
+// operand register holds -- no LDS table, no per-pair index arithmetic.  The
+// code layout of these modes keeps four codes byte-aligned (wq_layout.hpp).
+// ---------------------------------------------------------------------------
+struct RegTable {
+  uint32_t L[2], H[2];
+};
+
+// From 16-bit values packed in pairs P[j] = v[2j] | v[2j+1] << 16.
+template <int BITS>
+__device__ inline RegTable reg_table(const uint32_t* P) {
+  RegTable t;
+  t.L[0] = __builtin_amdgcn_perm(P[1], P[0], 0x06040200u);
+  t.H[0] = __builtin_amdgcn_perm(P[1], P[0], 0x07050301u);
+  if constexpr (BITS == 3) {
+    t.L[1] = __builtin_amdgcn_perm(P[3], P[2], 0x06040200u);
+    t.H[1] = __builtin_amdgcn_perm(P[3], P[2], 0x07050301u);
+  } else {
+    t.L[1] = t.L[0];
+    t.H[1] = t.H[0];
+  }
+  return t;
+}
+
+// Four codes of a 2- or 3-bit table layout, one per byte: elements
+// 4 HALF .. 4 HALF + 3 of k-block KB (see wq_layout.hpp).
+template <int BITS, int KB, int HALF>
+__device__ inline uint32_t table_codes4(const uint32_t* w) {
+  if constexpr (BITS == 2) {
+    return (w[KB / 2] >> (2 * (2 * (KB % 2) + HALF))) & 0x03030303u;
+  } else {
+    constexpr int x = 2 * KB + HALF;
+    if constexpr (x < 6) return (w[x / 2] >> (3 * (x % 2))) & 0x07070707u;
+    else if constexpr (x == 6) return ((w[0] >> 6) & 0x03030303u) | ((w[2] >> 4) & 0x04040404u);
+    else return ((w[1] >> 6) & 0x03030303u) | ((w[2] >> 5) & 0x04040404u);
+  }
+}
+
+// B operand of k-block KB from a register table: pair q = elements (2q, 2q+1).
+template <int BITS, int KB>
+__device__ inline u32x4 perm_table_frag(const uint32_t* w, const RegTable& t) {
+  u32x4 r;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const uint32_t x = half == 0 ? table_codes4<BITS, KB, 0>(w) : table_codes4<BITS, KB, 1>(w);
+    const uint32_t lo = __builtin_amdgcn_perm(t.L[1], t.L[0], x);
+    const uint32_t hi = __builtin_amdgcn_perm(t.H[1], t.H[0], x);
+    r[2 * half] = __builtin_amdgcn_perm(hi, lo, 0x05010400u);      // elements 4 half, 4 half + 1
+    r[2 * half + 1] = __builtin_amdgcn_perm(hi, lo, 0x07030602u);  // elements 4 half + 2, + 3
+  }
+  return r;
+}
+
+// Table values as pairs Tp[j] = T[2j] | T[2j+1] << 16 from lanes 0 .. 2^BITS - 1
+// holding T[lane] in their low 16 bits (every lane of the wave active).
+template <int BITS>
+__device__ inline void table_pairs_from_lanes(uint32_t tval, uint32_t* Tp) {
+#pragma unroll
+  for (int j = 0; j < (1 << BITS) / 2; ++j)
+    Tp[j] = ((uint32_t)__shfl((int)tval, 2 * j) & 0xFFFFu) | ((uint32_t)__shfl((int)tval, 2 * j + 1) << 16);
+}
+
+// ---------------------------------------------------------------------------
 // Offset decode: B operand (8 values of one k-block) for uniform modes.
 //   fp16: values are q - 2^(BITS-1)  (exact small integers)
 //   bf16: values are 128 + q         (exact; caller subtracts 128 + z later)
@@ -291,6 +359,7 @@ __device__ inline uint32_t fine_zero_bits(const uint32_t* zr, int kbu) {
 // ---------------------------------------------------------------------------
 template <int BITS, int KB, int COPIES = 32>
 __device__ inline u32x4 table_frag(const uint32_t* w, const uint32_t* tab) {
+  static_assert(BITS == 4, "2- and 3-bit table codes use register tables");
   u32x4 r;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -367,7 +436,25 @@ struct ExactParams {
   float sz;       // s * z (exact in fp32)
   h2 s_h;         // scale as an fp16 pair (fp16 fast paths)
   h2 nz_h;        // fp16 product path: -z (fp16 zero-points) or -(1024 + z) (integer zero-points)
+  RegTable rt;    // 2- and 3-bit table codes: the dequantised RN(s * T[q]) (scaled_reg_table)
 };
+
+// The dequantised values RN_dt(s * T[q]) of one (group, column) as a register
+// table, from the table pairs Tp: fp16 one packed product per pair (exact
+// product rounded once); bf16 the product in fp32 (exact) rounded once.
+template <int BITS, int DT>
+__device__ inline RegTable scaled_reg_table(const uint32_t* Tp, float s, const DecodeConsts& k) {
+  uint32_t P[(1 << BITS) / 2];
+#pragma unroll
+  for (int j = 0; j < (1 << BITS) / 2; ++j) {
+    const h2 v = as_h2(Tp[j]);
+    if constexpr (DT == F16)
+      P[j] = as_u32(v * h2s(s));
+    else
+      P[j] = pack2<DT>(__builtin_fmaf((float)v[0], s, k.nzero), __builtin_fmaf((float)v[1], s, k.nzero));
+  }
+  return reg_table<BITS>(P);
+}
 
 // Exact dequantised B operand for k-block KB: RN_dt(s*(q - z)) or RN_dt(s*T[q]).
 // tab: LDS fp16 pair table column for this lane (table mode only).
@@ -375,7 +462,9 @@ template <int BITS, int DT, int MODE, int KB, int COPIES = 32, bool SPLIT4 = tru
 __device__ inline u32x4 exact_frag(const uint32_t* w, const ExactParams& p, const uint32_t* tab,
                                    const DecodeConsts& k) {
   u32x4 r;
-  if constexpr (MODE == SYM && DT == F16) {
+  if constexpr (MODE == LUT && BITS < 4) {
+    return perm_table_frag<BITS, KB>(w, p.rt);
+  } else if constexpr (MODE == SYM && DT == F16) {
     // q - 2^(b-1) is exact in fp16; one fp16 multiply rounds s*(q-z) once.
     const u32x4 o = offset_frag<BITS, F16, KB>(w, k);
 #pragma unroll

@@ -76,10 +76,11 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
   // 128 x 128 tiles, whose 80 KiB of LDS (16 KiB table + two 32 KiB stages)
   // then leave room for two workgroups per CU.
   constexpr int COPIES = (TABLE && BITS == 4 && NT == 2) ? 16 : 32;
+  constexpr bool LDS_TABLE = TABLE && BITS == 4;  // 2/3-bit tables: register tables per group and column
   // one-shift nibble decode (bf16) except in 128 x 256 tiles, where its two
   // extra registers per column tile would spill
   constexpr bool SPLIT4 = !(BM == 128 && NT == 4);
-  __shared__ __attribute__((aligned(16))) uint32_t table[TABLE ? (COPIES << (2 * BITS)) : 4];
+  __shared__ __attribute__((aligned(16))) uint32_t table[LDS_TABLE ? (COPIES << (2 * BITS)) : 4];
   // Two stages of the BM x 128 activation tile, 16-byte chunks, row r at
   // chunk (c ^ (r % 16)).  Separate arrays so each stage's reads and loads are
   // distinct objects.
@@ -113,7 +114,12 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
   const uint32_t zp_lane = (uint32_t)((c >> 3) * ZREC + 4 * jg);
   const uint32_t zf_lane = FINE ? (uint32_t)((c * fine_per_unit(ZG > 0 ? ZG : 32) + h * ZPL) * 2) : 0u;
 
-  if constexpr (TABLE) fill_pair_table<BITS, false, COPIES>(table, a.lut, tid, 256);
+  if constexpr (LDS_TABLE) fill_pair_table<BITS, false, COPIES>(table, a.lut, tid, 256);
+  uint32_t Tp[4] = {0u, 0u, 0u, 0u};  // 2/3-bit tables: the values as pairs (lane i loads T[i])
+  if constexpr (TABLE && !LDS_TABLE) {
+    const uint32_t tv = __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(a.lut, 2u << BITS), (uint32_t)lane * 2u, 0, 0);
+    table_pairs_from_lanes<BITS>(tv, Tp);
+  }
   const uint32_t* tab = table + (lane % COPIES);
   const DecodeConsts dk = make_decode_consts<DT>();
 
@@ -238,6 +244,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
             prm[t].s_h = h2s(sv);
             prm[t].sz = MODE == LUT ? 0.0f : sv * z;
             prm[t].nz_h = h2s(MODE == ZERO_PACKED ? -(1024.0f + z) : -z);
+            if constexpr (TABLE && !LDS_TABLE) prm[t].rt = scaled_reg_table<BITS, DT>(Tp, sv, dk);
           }
         }
 #pragma unroll

@@ -80,6 +80,8 @@ __device__ inline u32x4 decode_frag(const uint32_t* w, const uint32_t* tab, cons
     } else {
       return exact_frag<BITS, DT, MODE, KB>(w, p, tab, k);
     }
+  } else if constexpr (MODE == LUT && BITS < 4) {
+    return perm_table_frag<BITS, KB>(w, p.rt);  // the layer's T[q] (p.rt unscaled here)
   } else if constexpr (MODE == LUT) {
     return table_frag<BITS, KB>(w, tab);
   } else if constexpr (MODE >= ZFINE) {
@@ -130,6 +132,8 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU, MR>() ? 512 : 1024)
   constexpr int WPL = BITS == 3 ? 3 : 4;
   constexpr int NXA = PK == 4 ? UPT : PK == 8 ? 2 * UPT : 4 * UPT;  // activation loads per tile
   constexpr bool TABLE = MODE == LUT;
+  constexpr bool LDS_TABLE = TABLE && BITS == 4;  // 4-bit: LDS pair table; 2/3-bit: register tables
+  constexpr bool REG_TABLE = TABLE && BITS < 4;
   constexpr bool Z16 = MODE == ZERO_F16;
   constexpr bool FINE = MODE >= ZFINE;          // fp16 zero-points per ZG rows
   constexpr int ZG = fine_zero_group(MODE);
@@ -142,7 +146,7 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU, MR>() ? 512 : 1024)
   constexpr int ZW = FINE ? (ZPL + 1) / 2 : 1;  // words of a lane's zero entry
   constexpr int NRED = PK == 4 ? 1 : PK == 8 ? 2 : 4;  // reduced values per lane per column tile
 
-  __shared__ __attribute__((aligned(16))) uint32_t table[TABLE ? (32 << (2 * BITS)) : 4];
+  __shared__ __attribute__((aligned(16))) uint32_t table[LDS_TABLE ? (32 << (2 * BITS)) : 4];
   // LDS of wave w at red + w * WSTRIDE: its activation stage (standard scheme,
   // 4 KiB) while it streams, then its partial results [TN][MR][NRED][64] for
   // the cross-wave reduction.
@@ -279,9 +283,17 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU, MR>() ? 512 : 1024)
     if constexpr (PACKED) __builtin_amdgcn_sched_barrier(0);
   }
 
-  if constexpr (TABLE) {
+  if constexpr (LDS_TABLE) {
     fill_pair_table_lanes<BITS>(table, lut_lane, threadIdx.x, a.waves * 64);  // fp16 values
     __syncthreads();
+  }
+  // 2- and 3-bit tables: the values as pairs, and (scale after the MFMA) the
+  // layer's table itself as a register table
+  uint32_t Tp[4] = {0u, 0u, 0u, 0u};
+  RegTable rt_raw = {};
+  if constexpr (REG_TABLE) {
+    table_pairs_from_lanes<BITS>(lut_lane, Tp);
+    if constexpr (!SCALED) rt_raw = reg_table<BITS>(Tp);
   }
   const uint32_t* tab = table + (lane & 31);
   const DecodeConsts dk = make_decode_consts<DT>();
@@ -335,10 +347,16 @@ __global__ __launch_bounds__((gemv_big_frames<BITS, TN, GPU, MR>() ? 512 : 1024)
   auto compute = [&](const Frame& f) __attribute__((always_inline)) {
     sfor<UPT>([&](auto uc) {
       constexpr int u = decltype(uc)::value;
-      ExactParams prm[TN];
+      ExactParams prm[TN] = {};
       if constexpr (SCALED) {
 #pragma unroll
-        for (int t = 0; t < TN; ++t) prm[t] = params(f, t, u);
+        for (int t = 0; t < TN; ++t) {
+          prm[t] = params(f, t, u);
+          if constexpr (REG_TABLE) prm[t].rt = scaled_reg_table<BITS, DT>(Tp, prm[t].s, dk);
+        }
+      } else if constexpr (REG_TABLE) {
+#pragma unroll
+        for (int t = 0; t < TN; ++t) prm[t].rt = rt_raw;
       }
       if constexpr (PK == 8) {
         // Two A operands per unit (p = 0, 1: rows 2m + j hold k-block 2p + j);
@@ -574,8 +592,8 @@ inline int pick_waves(const GemvArgs& g, int grid, bool table, int wmax, long pl
 }
 inline int pick_waves_auto(int grid, int ktiles, bool table, int wmax, long plain) {
   // about `plain` waves in flight (12288 when each workgroup fills an LDS code
-  // table, which caps the workgroups per CU), at most 32 k-tiles per wave,
-  // at least 2
+  // table -- 4-bit table codes -- which caps the workgroups per CU), at most
+  // 32 k-tiles per wave, at least 2
   const long target = table ? 12288L : plain;
   int w = 1;
   while (w < wmax && 2 * w <= ktiles && ((long)grid * w < target || ktiles > 32 * w)) w *= 2;
@@ -604,7 +622,7 @@ wq_status run_pf(GemvArgs g, int grid, hipStream_t s) {
 // occupancy.
 template <int DT, int BITS, int MODE, int TN, int GPU, bool SWIGLU, int MR>
 wq_status run_standard(GemvArgs g, int grid, hipStream_t s) {
-  constexpr bool stage = MR == 2 || !(MODE == LUT && TN == 4);
+  constexpr bool stage = MR == 2 || !(MODE == LUT && BITS == 4 && TN == 4);
   if constexpr (!stage) return run_pf<DT, BITS, MODE, TN, GPU, 0, SWIGLU, MR, false>(g, grid, s);
   else return run_pf<DT, BITS, MODE, TN, GPU, 0, SWIGLU, MR, true>(g, grid, s);
 }
@@ -619,7 +637,7 @@ wq_status pick_standard(GemvArgs g, hipStream_t s) {
     // size; measured faster than matching its per-wave work with workgroups
     // twice as large.
     const int wmax = gemv_big_frames<BITS, 1, GPU, MR>() ? 8 : 16;
-    const int kw = max(1, pick_waves(g, ntiles, MODE == LUT, wmax) / 2);  // waves per column tile
+    const int kw = max(1, pick_waves(g, ntiles, MODE == LUT && BITS == 4, wmax) / 2);  // waves per column tile
     g.waves = 2 * kw;
     g.kt_per_wave = (g.ktiles + kw - 1) / kw;
     return run_standard<DT, BITS, MODE, 1, GPU, true, MR>(g, ntiles / 2, s);
@@ -640,7 +658,7 @@ wq_status pick_standard(GemvArgs g, hipStream_t s) {
     // M = 9-16, unchanged where both fill alike; table codes keep four (their
     // two-tile variant stages the activations beside the LDS table: 20 %
     // slower).
-    if (MODE != LUT && tn == 4 && ntiles % 2 == 0) {
+    if (!(MODE == LUT && BITS == 4) && tn == 4 && ntiles % 2 == 0) {
       const long g4 = ntiles / 4, g2 = ntiles / 2;
       if (g2 * ((g4 + 255) / 256) > g4 * ((g2 + 255) / 256)) tn = 2;
     }
@@ -651,7 +669,7 @@ wq_status pick_standard(GemvArgs g, hipStream_t s) {
     // two row blocks: about half the waves, each streaming twice the k-range
     // (M = 32: 10-13 % faster on the 12288- and 22016-column layers, equal on
     // the others; at 16 rows the same target loses up to 10 %)
-    g.waves = pick_waves(g, grid, MODE == LUT, big ? 8 : 16, MR == 2 ? 1536L : 3072L);
+    g.waves = pick_waves(g, grid, MODE == LUT && BITS == 4, big ? 8 : 16, MR == 2 ? 1536L : 3072L);
     g.kt_per_wave = (g.ktiles + g.waves - 1) / g.waves;
     if constexpr (TNMAX >= 4)
       if (tn == 4) return run_standard<DT, BITS, MODE, 4, GPU, false, MR>(g, grid, s);
@@ -686,7 +704,7 @@ wq_status pick_shape(GemvArgs g, hipStream_t s) {
   const int wmax = gemv_big_frames<BITS, 1, GPU, 1>() ? 8 : 16;
   const bool pk8 = g.M > 4;
   if constexpr (SWIGLU) {
-    const int kw = max(1, pick_waves(g, ntiles, MODE == LUT, wmax) / 2);  // waves per column tile
+    const int kw = max(1, pick_waves(g, ntiles, MODE == LUT && BITS == 4, wmax) / 2);  // waves per column tile
     g.waves = 2 * kw;
     g.kt_per_wave = (g.ktiles + kw - 1) / kw;
     return pk8 ? run_pf<DT, BITS, MODE, 1, GPU, 8, true, 1>(g, ntiles / 2, s)
@@ -698,7 +716,7 @@ wq_status pick_shape(GemvArgs g, hipStream_t s) {
     // (two column tiles per wave, sharing the activation loads and, for table
     // codes, the LDS table fill of half as many workgroups, measured 3-35 %
     // slower on every M = 1 layer of the workloads)
-    g.waves = pick_waves(g, ntiles, MODE == LUT, wmax, 6144L);
+    g.waves = pick_waves(g, ntiles, MODE == LUT && BITS == 4, wmax, 6144L);
     g.kt_per_wave = (g.ktiles + g.waves - 1) / g.waves;
     return pk8 ? run_pf<DT, BITS, MODE, 1, GPU, 8, false, 1>(g, ntiles, s)
                : run_pf<DT, BITS, MODE, 1, GPU, 4, false, 1>(g, ntiles, s);

@@ -26,10 +26,17 @@
 //                  two 16-bit halves, so one AND/OR makes two fp16 values)
 //   4-bit table    word kb, nibble e               (a byte is a code pair)
 //   2-bit uniform  word kb/2, bits 16*(e%2) + 2*i,  i = 4*(kb%2) + e/2
-//   2-bit table    word kb/2, bits 4*i + 2*(e%2)    (a nibble is a code pair)
-//   3-bit (both)   pair p = 4*kb + e/2 is the 6-bit field lo | hi << 3
+//   2-bit table    word kb/2, bits 8*(e%4) + 2*(2*(kb%2) + e/4)
+//                  (elements 4j .. 4j + 3 of a k-block sit in the four bytes
+//                  at one shift: one AND isolates four codes, one per byte)
+//   3-bit uniform  pair p = 4*kb + e/2 is the 6-bit field lo | hi << 3
 //                  (lo = even element); pairs 0..14 at bits 6*(p%5) of word
 //                  p/5, pair 15 split over bits 30..31 of words 0, 1, 2.
+//   3-bit table    group x = 2*kb + e/4 of four codes, byte b = e%4: groups
+//                  0..5 at bits 8b + 3*(x%2) of word x/2; groups 6 and 7 keep
+//                  their low two bits at bits 8b + 6 of word x - 6 and their
+//                  high bit at bit 8b + x of word 2 (four codes, one per
+//                  byte, from one or two shifts and masks).
 //
 // Scales / zero-points.  With GPU = groups per 128-row unit (1 for groups of
 // 128 rows or more, else 128 / group_size) and a record per (column tile,
