@@ -255,9 +255,11 @@ def read_ceiling(stream, bufs, nbytes, n):
 
 def run_profile_cases(args):
     """Only the named products (and an optional device copy of known size),
-    each launched --profile-reps times back to back over rotated copies of its
-    layer: the workload of the committed rocprofv3 summaries, one process per
-    counter pass, so every dispatch of a kernel in the run belongs to one case."""
+    each warmed up (warm_up) and then launched --profile-reps times back to
+    back over rotated copies of its layer: the workload of the committed
+    rocprofv3 summaries, one process per counter pass, so every dispatch of a
+    kernel in the run belongs to one case (the summaries keep the last
+    --profile-reps dispatches of each kernel)."""
     import torch
 
     import workloads as wl
@@ -291,6 +293,8 @@ def run_profile_cases(args):
         for i in range(R):
             wq.linear(x, copies[i], out=y, ws=ws, stream=stream)
         torch.cuda.synchronize()
+        # clocks up first; the summaries keep the last --profile-reps dispatches
+        warm_up(stream, lambda: [wq.linear(x, copies[i], out=y, ws=ws, stream=stream) for i in range(R)])
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
