@@ -213,13 +213,32 @@ __global__ __launch_bounds__(64) void dequant_debug_kernel(const uint8_t* __rest
   });
 }
 
-// Act-order: xp[m][i] = x[m][perm[i]].
+// Act-order: xp[m][i] = x[m][perm[i]].  Eight consecutive i per thread: two
+// 16-byte loads of perm, eight independent 2-byte loads of x, one 16-byte
+// store (K % 8 == 0, perm and xp 16-byte aligned, M * K < 2^31: checked by
+// the caller).
+__global__ void gather_x8_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ perm, int M, int K,
+                                 uint16_t* __restrict__ xp) {
+  const int k8 = K >> 3;
+  const unsigned t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= (unsigned)M * (unsigned)k8) return;
+  const unsigned m = t / (unsigned)k8, i = (t - m * (unsigned)k8) * 8u;
+  const int4 p0 = *(const int4*)(perm + i), p1 = *(const int4*)(perm + i + 4);
+  const uint16_t* xr = x + (size_t)m * K;
+  uint4 v;
+  v.x = (uint32_t)xr[p0.x] | ((uint32_t)xr[p0.y] << 16);
+  v.y = (uint32_t)xr[p0.z] | ((uint32_t)xr[p0.w] << 16);
+  v.z = (uint32_t)xr[p1.x] | ((uint32_t)xr[p1.y] << 16);
+  v.w = (uint32_t)xr[p1.z] | ((uint32_t)xr[p1.w] << 16);
+  *(uint4*)(xp + (size_t)m * K + i) = v;
+}
+// The same one element per thread (any alignment of perm).
 __global__ void gather_x_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ perm, int M, int K,
                                 uint16_t* __restrict__ xp) {
-  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (size_t)M * K) return;
-  const size_t m = i / K, k = i % K;
-  xp[i] = x[m * K + perm[k]];
+  const unsigned i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (unsigned)M * (unsigned)K) return;
+  const unsigned m = i / (unsigned)K, k = i - m * (unsigned)K;
+  xp[i] = x[(size_t)m * K + perm[k]];
 }
 
 // ---------------------------------------------------------------------------
@@ -400,9 +419,13 @@ static wq_status product(bool gemm, bool swiglu, const void* x, wq_dtype dt, con
   hipStream_t s = (hipStream_t)stream;
   const void* xin = x;
   if (perm) {
-    const size_t total = (size_t)M * K;
-    hipLaunchKernelGGL(gather_x_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
-                       (const uint16_t*)x, perm, M, K, (uint16_t*)ws);
+    const size_t total = (size_t)M * K;  // < 2^30 (activation buffer check above)
+    if (K % 8 == 0 && ((uintptr_t)perm & 15) == 0)
+      hipLaunchKernelGGL(gather_x8_kernel, dim3((unsigned)((total / 8 + 255) / 256)), dim3(256), 0, s,
+                         (const uint16_t*)x, perm, M, K, (uint16_t*)ws);
+    else
+      hipLaunchKernelGGL(gather_x_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
+                         (const uint16_t*)x, perm, M, K, (uint16_t*)ws);
     if ((st = launch_status()) != WQ_OK) return st;
     xin = ws;
   }
