@@ -109,3 +109,32 @@ def test_hadamard_checks():
         wq.wq_hadamard(x, 128, out=torch.zeros((2, 256), dtype=torch.bfloat16))
     with pytest.raises(ValueError, match="GPU tensor"):
         wq.wq_hadamard(x, 128)
+
+
+def test_layer_checks(layer):
+    x = x_of(1, layer)
+    short = wq.PackedLayer(layer.packed[:-256], layer.K, layer.N, 4, 128, wq.SYM)
+    with pytest.raises(ValueError, match="shorter than the packed size"):
+        wq.wq_gemv(x, short)
+    with pytest.raises(ValueError, match="shorter than the packed size"):
+        wq.wq_dequant_debug(short, torch.float16)
+    wide = wq.PackedLayer(layer.packed, layer.K, layer.N + 16, 4, 128, wq.SYM)
+    with pytest.raises(ValueError, match="shorter than the packed size"):
+        wq.wq_gemm(x_of(1, wide), wide)
+    bad_perm = wq.PackedLayer(layer.packed, layer.K, layer.N, 4, 128, wq.SYM,
+                              perm=torch.arange(layer.K, dtype=torch.int64))
+    with pytest.raises(ValueError, match="layer.perm must have dtype"):
+        wq.wq_gemv(x, bad_perm)
+    short_perm = wq.PackedLayer(layer.packed, layer.K, layer.N, 4, 128, wq.SYM,
+                                perm=torch.arange(layer.K - 1, dtype=torch.int32))
+    with pytest.raises(ValueError, match="layer.perm must have shape"):
+        wq.wq_gemm(x, short_perm)
+    no_lut = wq.PackedLayer(torch.zeros(wq.wq_packed_bytes(layer.K, layer.N, 4, 128, wq.LUT), dtype=torch.uint8),
+                            layer.K, layer.N, 4, 128, wq.LUT)
+    with pytest.raises(ValueError, match="table is needed"):
+        wq.wq_gemv(x, no_lut)
+    with pytest.raises(ValueError, match="layer.packed must be"):
+        wq.wq_gemv(x, wq.PackedLayer(layer.packed.view(torch.int8), layer.K, layer.N, 4, 128, wq.SYM))
+    out = torch.empty((1, layer.N), dtype=torch.float16)
+    with pytest.raises(ValueError, match="shorter than the packed size"):
+        wq.wq_gemm_noalloc(x, short, out)

@@ -325,3 +325,26 @@ def test_degenerate_values(orc, wq, fn, M):
     LK = wl.Layer(K, N, 4, K, wl.SYM, Lg.qweight, Lg.scales)
     assert torch.equal(getattr(wq, fn)(x, repack_layer(wq, Lg)), getattr(wq, fn)(x, repack_layer(wq, LK)))
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("fn,M", [("wq_gemv", 1), ("wq_gemv", 7), ("wq_gemm", 40)])
+def test_act_order_gather_forms_agree(orc, wq, fn, M):
+    """The act-order gather runs eight elements per thread when perm is
+    16-byte aligned and one per thread otherwise; both give the same output
+    bit for bit, and it meets the oracle."""
+    import dataclasses
+    L = make(wl.ZERO_PACKED, 4, 32, 1024, 96, 91, act_order=True)
+    layer = repack_layer(wq, L)
+    assert layer.perm.data_ptr() % 16 == 0
+    buf = torch.empty(layer.K + 1, dtype=torch.int32, device=layer.perm.device)
+    buf[1:] = layer.perm
+    odd = dataclasses.replace(layer, perm=buf[1:])
+    assert odd.perm.data_ptr() % 16 == 4
+    x_bits = wl.make_x(M, L.K, wl.BF16, 31 + M)
+    x = bits_to_tensor(x_bits, torch.bfloat16, "cuda")
+    y8, y1 = getattr(wq, fn)(x, layer), getattr(wq, fn)(x, odd)
+    torch.cuda.synchronize()
+    assert torch.equal(y8.view(torch.int16), y1.view(torch.int16))
+    cols = np.arange(L.N, dtype=np.int32)
+    ok, err, bound = within_tolerance(tensor_f64(y8), oracle_y(orc, x_bits, wl.BF16, L, cols))
+    assert ok, f"max error {err:.3e} > bound {bound:.3e}"

@@ -211,8 +211,26 @@ def wq_repack_gate_up(qweight: torch.Tensor, scales: torch.Tensor, zeros: Option
                    stream)
 
 
+def _check_layer(layer: PackedLayer, dev):
+    """The layer's buffers as the kernels read them: the packed buffer at least
+    wq_packed_bytes long, the table fp16 [2^bits], the permutation int32 [K],
+    all contiguous and on `dev`."""
+    p = layer.packed
+    _need(isinstance(p, torch.Tensor) and p.dtype == torch.uint8 and p.dim() == 1 and p.is_contiguous(),
+          "layer.packed must be a contiguous 1-D uint8 tensor")
+    _need(p.device == dev, "x and the layer must be on the same device")
+    _need(p.numel() >= wq_packed_bytes(layer.K, layer.N, layer.bits, layer.group_size, layer.mode),
+          "layer.packed is shorter than the packed size of the layer it describes")
+    _need((layer.lut is not None) == (layer.mode == LUT), "a table is needed exactly in table mode")
+    if layer.lut is not None:
+        _check_tensor(layer.lut, "layer.lut", (torch.float16,), (1 << layer.bits,), dev)
+    if layer.perm is not None:
+        _check_tensor(layer.perm, "layer.perm", (torch.int32,), (layer.K,), dev)
+
+
 def wq_dequant_debug(layer: PackedLayer, dtype: torch.dtype, stream=None) -> torch.Tensor:
     _dt(dtype)
+    _check_layer(layer, layer.packed.device)
     _check_cuda(layer.packed, "layer.packed")
     w = torch.empty((layer.K, layer.N), dtype=dtype, device=layer.packed.device)
     rc = lib().wq_dequant_debug(_ptr(layer.packed), layer.mode, _ptr(layer.lut), _ptr(layer.perm),
@@ -243,12 +261,8 @@ def _product(fn: str, x: torch.Tensor, layer: PackedLayer, out: Optional[torch.T
         _need(isinstance(ws, torch.Tensor) and ws.is_contiguous() and ws.device == x.device,
               "ws must be a contiguous tensor on the device of x")
         _need(ws.numel() * ws.element_size() >= need, lambda: f"ws holds fewer than the {need} bytes this call needs")
-    _need(layer.packed.device == x.device, "x and the layer must be on the same device")
+    _check_layer(layer, x.device)
     _check_cuda(x, "x")
-    if layer.lut is not None:
-        _need(layer.lut.device == x.device, "the layer's table must be on the device of x")
-    if layer.perm is not None:
-        _need(layer.perm.device == x.device and layer.perm.numel() == layer.K, "bad layer.perm")
     if out is None:
         out = torch.empty((M, ncols), dtype=x.dtype, device=x.device)
     if need and ws is None:
@@ -282,7 +296,7 @@ def wq_gemm_noalloc(x: torch.Tensor, layer: PackedLayer, out: torch.Tensor, stre
           "x must be a contiguous [M][K] tensor")
     _dt(x.dtype)
     _check_tensor(out, "out", (x.dtype,), (x.shape[0], layer.N), x.device)
-    _need(layer.packed.device == x.device, "x and the layer must be on the same device")
+    _check_layer(layer, x.device)
     _check_cuda(x, "x")
     rc = lib().wq_gemm_noalloc(_ptr(x), _dt(x.dtype), _ptr(layer.packed), layer.mode, _ptr(layer.lut),
                                _ptr(layer.perm), _ptr(out), x.shape[0], layer.N, layer.K, layer.bits,

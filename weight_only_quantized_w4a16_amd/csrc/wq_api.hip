@@ -348,9 +348,12 @@ static wq_status repack(const uint32_t* qweight, const uint16_t* scales, const v
       hipLaunchKernelGGL(repack_zeros_packed_kernel<2>, g2, dim3(256), 0, s, (const uint32_t*)zeros, N, L.nrec,
                          L.gpu, L.ntiles, gate_up, (uint32_t*)(out + L.zeros_off));
   }
-  if ((st = launch_status()) != WQ_OK) return st;
-  // host_perm is read by the copy above: wait before it goes out of scope.
-  return hipStreamSynchronize(s) == hipSuccess ? WQ_OK : WQ_EHIP;
+  st = launch_status();
+  // host_perm is read by the copy above: wait before it goes out of scope,
+  // also when a launch failed.
+  const bool synced = hipStreamSynchronize(s) == hipSuccess;
+  if (st != WQ_OK) return st;
+  return synced ? WQ_OK : WQ_EHIP;
 }
 
 wq_status wq_repack(const uint32_t* qweight, const uint16_t* scales, const void* zeros, wq_qmode mode,
