@@ -6,7 +6,8 @@
 // reply).  So this kernel is built around one stream of the packed weight:
 //
 //  * A workgroup owns TN column tiles (16 columns each) and the whole of K;
-//    its waves (1..16, about 16 per CU over the grid) split K and each streams
+//    its waves (1..16; a few thousand over the grid, see the launch-shape
+//    choice below) split K and each streams
 //    its k-range of those tiles PF tiles ahead with 128-bit coalesced buffer
 //    loads, 1 KiB per wave per tile.  Loads past the range are issued with an
 //    out-of-range offset instead of a branch, so the code stays straight-line
