@@ -73,9 +73,18 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _stream(stream) -> ctypes.c_void_p:
+def _stream(stream, dev: torch.device) -> ctypes.c_void_p:
+    """The stream to launch on: `stream`, or the current stream of `dev`.  The
+    library works on the current HIP device (its scratch array is per device),
+    so that must be the device of the tensors."""
+    cur = torch.cuda.current_device()
+    if dev.index != cur:
+        raise ValueError(f"the tensors are on {dev} but the current device is cuda:{cur}; "
+                         f"call under torch.cuda.device({dev})")
     if stream is None:
-        stream = torch.cuda.current_stream()
+        stream = torch.cuda.current_stream(dev)
+    elif stream.device != dev:
+        raise ValueError(f"stream belongs to {stream.device}, the tensors to {dev}")
     return ctypes.c_void_p(stream.cuda_stream)
 
 
@@ -188,7 +197,7 @@ def _repack(fn: str, qweight, scales, zeros, mode, g_idx, K, N, bits, group_size
         perm = torch.empty(K, dtype=torch.int32, device=dev)
     rc = getattr(lib(), fn)(_ptr(qweight), _ptr(scales), _ptr(zeros), mode,
                             None if g_host is None else ctypes.c_void_p(g_host.ctypes.data),
-                            K, N, bits, group_size, _ptr(packed), _ptr(perm), _stream(stream))
+                            K, N, bits, group_size, _ptr(packed), _ptr(perm), _stream(stream, dev))
     _check(fn, rc)
     return PackedLayer(packed, K, N, bits, group_size, mode, lut, perm, fn == "wq_repack_gate_up")
 
@@ -235,7 +244,7 @@ def wq_dequant_debug(layer: PackedLayer, dtype: torch.dtype, stream=None) -> tor
     w = torch.empty((layer.K, layer.N), dtype=dtype, device=layer.packed.device)
     rc = lib().wq_dequant_debug(_ptr(layer.packed), layer.mode, _ptr(layer.lut), _ptr(layer.perm),
                                 layer.K, layer.N, layer.bits, layer.group_size, _dt(dtype), _ptr(w),
-                                _stream(stream))
+                                _stream(stream, w.device))
     _check("wq_dequant_debug", rc)
     return w
 
@@ -269,7 +278,7 @@ def _product(fn: str, x: torch.Tensor, layer: PackedLayer, out: Optional[torch.T
         ws = torch.empty(need, dtype=torch.uint8, device=x.device)
     rc = getattr(lib(), fn)(_ptr(x), _dt(x.dtype), _ptr(layer.packed), layer.mode, _ptr(layer.lut),
                             _ptr(layer.perm), _ptr(out), M, layer.N, layer.K, layer.bits, layer.group_size,
-                            _ptr(ws) if need else None, need if need else 0, _stream(stream))
+                            _ptr(ws) if need else None, need if need else 0, _stream(stream, x.device))
     _check(fn, rc)
     return out
 
@@ -300,7 +309,7 @@ def wq_gemm_noalloc(x: torch.Tensor, layer: PackedLayer, out: torch.Tensor, stre
     _check_cuda(x, "x")
     rc = lib().wq_gemm_noalloc(_ptr(x), _dt(x.dtype), _ptr(layer.packed), layer.mode, _ptr(layer.lut),
                                _ptr(layer.perm), _ptr(out), x.shape[0], layer.N, layer.K, layer.bits,
-                               layer.group_size, _stream(stream))
+                               layer.group_size, _stream(stream, x.device))
     _check("wq_gemm_noalloc", rc)
     return out
 
@@ -327,7 +336,7 @@ def wq_hadamard(x: torch.Tensor, block: int, out: Optional[torch.Tensor] = None,
     elif out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous() or out.device != x.device:
         raise ValueError("out must be a contiguous tensor like x, on its device")
     _check_cuda(x, "x")
-    rc = lib().wq_hadamard(_ptr(x), _dt(x.dtype), _ptr(out), M, K, block, _stream(stream))
+    rc = lib().wq_hadamard(_ptr(x), _dt(x.dtype), _ptr(out), M, K, block, _stream(stream, x.device))
     _check("wq_hadamard", rc)
     return out
 
