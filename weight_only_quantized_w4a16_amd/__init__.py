@@ -35,7 +35,7 @@ class WQError(RuntimeError):
 
 
 def lib() -> ctypes.CDLL:
-    """Load libwq.so (built by __graft_entry__.build() or weight_only_quantized_w4a16_amd/build.py)."""
+    """Load libwq.so (built by weight_only_quantized_w4a16_amd/build.py)."""
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
