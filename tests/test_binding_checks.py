@@ -138,3 +138,16 @@ def test_layer_checks(layer):
     out = torch.empty((1, layer.N), dtype=torch.float16)
     with pytest.raises(ValueError, match="shorter than the packed size"):
         wq.wq_gemm_noalloc(x, short, out)
+
+
+def test_linear_dispatch():
+    """linear() sends decode-sized M to the GEMV, except where the large-M
+    product was measured faster: table codes above 16 rows at 2 bits, and at
+    4 bits on layers wider than 16384 columns."""
+    def lay(bits, N, mode=wq.LUT):
+        return wq.PackedLayer(None, 8192, N, bits, 64, mode)
+    assert wq.use_gemv(1, lay(4, 28672)) and wq.use_gemv(16, lay(4, 28672))
+    assert not wq.use_gemv(17, lay(4, 28672)) and not wq.use_gemv(32, lay(4, 28672))
+    assert wq.use_gemv(32, lay(4, 8192)) and wq.use_gemv(32, lay(3, 28672))
+    assert wq.use_gemv(16, lay(2, 8192)) and not wq.use_gemv(17, lay(2, 8192))
+    assert wq.use_gemv(32, lay(4, 53248, wq.ZERO_PACKED)) and not wq.use_gemv(33, lay(4, 4096, wq.SYM))

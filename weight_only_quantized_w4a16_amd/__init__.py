@@ -343,16 +343,22 @@ def wq_hadamard(x: torch.Tensor, block: int, out: Optional[torch.Tensor] = None,
 
 # Largest M that linear() sends to wq_gemv (which takes M <= 32).  Measured on
 # MI355X over the LLaMA-7B/70B/405B layer shapes (graph-replayed, rotated
-# copies): the GEMV beats the tiled GEMM at M = 24 and 32 on every shape and
-# code width, except 2-bit table layers above 16 rows, whose second block of
-# rows takes a second pass over the weights.
+# copies): the GEMV beats the tiled GEMM at M = 17-32 on every shape and code
+# width but two.  2-bit table layers take a second pass over the weights for
+# rows 16-31.  4-bit table layers hold 64 KiB of LDS per workgroup above 16
+# rows (the pair table and the activation stages), so two workgroups fit per
+# CU, and with more than 1024 column tiles the grid needs a second round: on
+# the 8192 x 28672 layer the GEMM is 13-17 % faster at M = 17-32, while on
+# 28672 x 8192 the GEMV stays 5-6 % ahead.
 GEMV_MAX_M = 32
+_LUT4_GEMV_MAX_N = 16384  # 1024 column tiles
 
 
 def use_gemv(M: int, layer: PackedLayer) -> bool:
     """Whether linear() sends an M-row product with this layer to the GEMV."""
-    if layer.bits == 2 and layer.mode == LUT:
-        return M <= 16
+    if layer.mode == LUT and M > 16:
+        if layer.bits == 2 or (layer.bits == 4 and layer.N > _LUT4_GEMV_MAX_N):
+            return False
     return M <= GEMV_MAX_M
 
 
